@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for one round of draft-token verification.
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import it.  Shares no code with the HIP path.
+"""
+from .verify import (verify_batch, verify_request, tempered_softmax, lowest_argmax,
+                     keeps_draft, positive_residual, inverse_cdf, widen_temperature)
+from .cost_model import time_per_token, expected_progress
+
+__all__ = ["verify_batch", "verify_request", "tempered_softmax", "lowest_argmax",
+           "keeps_draft", "positive_residual", "inverse_cdf", "widen_temperature",
+           "time_per_token", "expected_progress"]

@@ -1,0 +1,316 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each pin is a plain function taking the oracle's `verify` module, so the same
+checks run on the oracle as written (tests/test_oracle_pins.py) and on copies
+with a planted mistake (tests/test_oracle_mutants.py), which must fail at least
+one pin.  Nothing here retypes the oracle's formulas: expectations come from
+the pages' worked examples, hand-derived closed forms, scipy / numpy routines
+the oracle does not call, and exact statistics of the construction.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _logits_from_probs(rows) -> np.ndarray:
+    p = np.asarray(rows, dtype=np.float64)
+    out = np.full(p.shape, -1000.0)
+    pos = p > 0
+    out[pos] = np.log(p[pos])
+    return out
+
+
+def _run(vm, target, draft, tokens, greedy, T, u, w):
+    return vm.verify_request(np.asarray(target, np.float64),
+                             None if draft is None else np.asarray(draft, np.float64),
+                             np.asarray(tokens), greedy, T, np.asarray(u, np.float64), w)
+
+
+# ---------------------------------------------------------------- worked examples
+def pin_abr_example(vm):
+    """A B C D -> A B R for every uniform that rejects C ([CZ] section 1)."""
+    g = load_golden("abr_example.json")
+    voc = {s: i for i, s in enumerate(g["vocab"])}
+    tgt = _logits_from_probs(g["target_probs"])
+    dr = _logits_from_probs(g["draft_probs"])
+    toks = [voc[s] for s in g["draft_tokens"]]
+    thr = g["reject_threshold_C"]
+    grid = [0.0, 0.1, 0.37, 0.5, 0.8, 0.999]
+    for uA in grid:
+        for uC in [thr + 1e-6, 0.3, 0.6, 0.99]:
+            for w in [0.0, 0.2, 0.5, 0.9, 0.9999]:
+                r = _run(vm, tgt, dr, toks, False, g["temperature"], [uA, 1.0 - uA, uC, 0.0], w)
+                assert r["a"] == g["expected"]["accepted_len"], (uA, uC, w, r)
+                assert r["committed"] == [voc[s] for s in g["expected"]["committed"]], (uA, uC, w, r)
+    # a uniform below p/q keeps C, so the round goes on past position 2
+    r = _run(vm, tgt, dr, toks, False, 1.0, [0.5, 0.5, thr - 1e-6, 0.99], 0.5)
+    assert r["a"] >= 3 and r["committed"][:3] == toks[:3], r
+    # k = 2: both drafts survive and the bonus comes from target row 2 by inverse CDF
+    tk = g["truncated_k2_expected"]
+    for w, name in tk["bonus_for_w"]:
+        r = _run(vm, tgt[:3], dr[:2], toks[:2], False, 1.0, [0.9, 0.9], w)
+        assert r["a"] == tk["accepted_len"], r
+        assert r["committed"] == toks[:2] + [voc[name]], (w, r)
+
+
+def pin_weather_example(vm):
+    """Greedy: sunny and warm outside -> sunny and clear ([VLLM] accept/reject example)."""
+    g = load_golden("weather_example.json")
+    voc = {s: i for i, s in enumerate(g["vocab"])}
+    toks = [voc[s] for s in g["draft_tokens"]]
+    r = _run(vm, g["target_logits"], None, toks, True, None, [0.0] * 4, 0.0)
+    assert r["a"] == g["expected"]["accepted_len"], r
+    assert r["committed"] == [voc[s] for s in g["expected"]["committed"]], r
+
+
+def pin_t1_t4_round(vm):
+    """T1 T2 T3 T4, check check cross: commit T1 T2 + replacement from [p-q]_+ ([HN], [CZ] s.1)."""
+    g = load_golden("round_t1_t4.json")
+    voc = {s: i for i, s in enumerate(g["vocab"])}
+    tgt = _logits_from_probs(g["target_probs"])
+    dr = _logits_from_probs(g["draft_probs"])
+    toks = [voc[s] for s in g["draft_tokens"]]
+    for uC in [0.2 + 1e-6, 0.5, 0.95]:
+        for w, name in g["expected"]["replacement_for_w"]:
+            r = _run(vm, tgt, dr, toks, False, 1.0, [0.99, 0.99, uC, 0.0], w)
+            assert r["a"] == g["expected"]["accepted_len"], r
+            assert r["committed"] == [voc[s] for s in g["expected"]["committed_prefix"]] + [voc[name]], (uC, w, r)
+
+
+def pin_greedy_ties(vm):
+    """Lowest id wins a tied maximum (the library's reading of greedy equivalence)."""
+    g = load_golden("greedy_ties.json")
+    for c in g["cases"]:
+        r = _run(vm, g["target_logits"], None, c["draft_tokens"], True, None, [0.0, 0.0], 0.0)
+        assert r["a"] == c["accepted_len"] and r["committed"] == c["committed"], (c, r)
+
+
+# ---------------------------------------------------------------- closed forms
+def _rows(rng, V, k, sigma=1.5, noise=1.0):
+    z = rng.normal(0.0, sigma, size=(k + 1, V))
+    d = z[:k] + rng.normal(0.0, noise, size=(k, V))
+    return z, d
+
+
+def pin_exact_distribution_quadrature(vm, G: int = 1024):
+    """V = 3, k = 1: with y ~ q enumerated exactly and (u, w) swept over a 1/G grid of
+    midpoints, the committed token's frequency equals p (the target-distribution
+    guarantee of [CZ] section 1) within the grid resolution; k = 0 gives p too."""
+    rng = np.random.default_rng(7)
+    grid = (np.arange(G) + 0.5) / G
+    for T in (1.0, 0.7):
+        z, d = _rows(rng, 3, 1)
+        p = scipy.special.softmax(z[0] / np.float32(T))
+        q = scipy.special.softmax(d[0] / np.float32(T))
+        # acceptance frequency for each possible draft, from the u sweep
+        acc = np.zeros(3)
+        for y in range(3):
+            acc[y] = np.mean([_run(vm, z, d, [y], False, T, [u], 0.5)["a"] == 1 for u in grid])
+            assert abs(acc[y] - min(1.0, p[y] / q[y])) <= 1.0 / G + 1e-12, (y, acc[y], p[y] / q[y])
+        # correction distribution, from the w sweep with a rejecting uniform
+        y_rej = int(np.argmin(p / q))
+        corr = np.zeros(3)
+        for w in grid:
+            r = _run(vm, z, d, [y_rej], False, T, [0.999999], w)
+            assert r["a"] == 0
+            corr[r["committed"][0]] += 1.0 / G
+        freq = np.zeros(3)
+        for y in range(3):
+            freq[y] += q[y] * acc[y]
+            freq += q[y] * (1.0 - acc[y]) * corr
+        assert np.all(np.abs(freq - p) <= 3.0 / G), (freq, p)
+        # k = 0: the bonus alone is a draw from p
+        bon = np.zeros(3)
+        for w in grid:
+            bon[_run(vm, z[1:], d[:0], [], False, T, [], w)["committed"][0]] += 1.0 / G
+        pb = scipy.special.softmax(z[1] / np.float32(T))
+        assert np.all(np.abs(bon - pb) <= 1.0 / G + 1e-12), (bon, pb)
+
+
+def pin_monte_carlo(vm, trials: int = 12000, cases=((2, 1), (3, 3), (8, 1), (16, 3)), seed=11):
+    """Monte Carlo against the closed forms of [CZ] sections 1 and 5:
+    * the first committed token and the token at position j (given position j is
+      reached) are distributed as p_j;
+    * P(A >= j) = prod_{i<j} beta_i with beta_i = sum_v min(p_i, q_i);
+    * E[A] + 1 equals DSpark's progress 1 + sum_j s_j with c_i = beta_i.
+    Every cell must lie within 5 sigma of its expectation."""
+    from oracle.cost_model import expected_progress
+    rng = np.random.default_rng(seed)
+    T = 0.9
+    for V, k in cases:
+        z, d = _rows(rng, V, k)
+        P = [scipy.special.softmax(z[i] / np.float32(T)) for i in range(k + 1)]
+        Q = [scipy.special.softmax(d[i] / np.float32(T)) for i in range(k)]
+        beta = [float(np.minimum(P[i], Q[i]).sum()) for i in range(k)]
+        A = np.zeros(trials, np.int64)
+        first = np.zeros(V)
+        at_pos = [np.zeros(V) for _ in range(k + 1)]
+        for n in range(trials):
+            ys = [int(rng.choice(V, p=Q[i])) for i in range(k)]
+            u = rng.random(k)
+            w = rng.random()
+            r = _run(vm, z, d, ys, False, T, u, w)
+            A[n] = r["a"]
+            first[r["committed"][0]] += 1
+            for j, t in enumerate(r["committed"]):
+                at_pos[j][t] += 1
+        def close(count, n, prob):
+            return abs(count - n * prob) <= 5.0 * math.sqrt(n * prob * (1 - prob)) + 1.0
+        assert all(close(first[v], trials, P[0][v]) for v in range(V)), (V, k, first / trials, P[0])
+        for j in range(1, k + 1):
+            surv = float(np.prod(beta[:j]))
+            assert close(int((A >= j).sum()), trials, surv), (V, k, j, (A >= j).mean(), surv)
+            reached = int((A >= j).sum())
+            if reached > 200:
+                assert all(close(at_pos[j][v], reached, P[j][v]) for v in range(V)), (V, k, j)
+        mean_prog = expected_progress(beta, k)
+        sd = math.sqrt(max(np.var(A), 1e-12) / trials)
+        assert abs(A.mean() + 1.0 - mean_prog) <= 5.0 * sd + 1e-9, (A.mean() + 1, mean_prog)
+
+
+# ---------------------------------------------------------------- special cases
+def pin_special_cases(vm):
+    rng = np.random.default_rng(3)
+    V = 40
+    z, d = _rows(rng, V, 3)
+    T = 0.8
+    # softmax equals scipy's at the fp32-widened temperature
+    for TT in (0.25, 0.7, 1.0, 1.9):
+        ref = scipy.special.softmax(z[0] / float(np.float32(TT)))
+        got = vm.tempered_softmax(z[0], vm.widen_temperature(TT))
+        assert np.allclose(got, ref, rtol=1e-13, atol=0), TT
+    # k = 0: the bonus is inverse-CDF sampling of p (numpy searchsorted, side='right')
+    p = scipy.special.softmax(z[0] / np.float32(T))
+    F = np.cumsum(p)
+    for w in np.linspace(0.0, 0.999, 97):
+        if np.min(np.abs(F - w)) < 1e-9:
+            continue
+        want = int(np.searchsorted(F, w, side="right"))
+        got = _run(vm, z[:1], d[:0], [], False, T, [], float(w))["committed"][0]
+        assert got == want, (w, got, want)
+    # q == p: every draft survives for any u < 1, then a bonus from the last row
+    y = [3, 7, 11]
+    r = _run(vm, z, z[:3].copy(), y, False, T, [0.999999, 0.999999, 0.999999], 0.3)
+    assert r["a"] == 3 and r["committed"][:3] == y, r
+    # q one-hot at y: y survives iff u < p(y); the correction is p with y removed
+    onehot = np.full((1, V), -1000.0)
+    onehot[0, 5] = 0.0
+    p0 = scipy.special.softmax(z[0] / np.float32(T))
+    for u in (0.5 * p0[5], 1.5 * p0[5], 0.9):
+        r = _run(vm, z[:2], onehot, [5], False, T, [u], 0.4)
+        assert (r["a"] == 1) == (u < p0[5]), (u, p0[5], r)
+    rest = p0.copy()
+    rest[5] = 0.0
+    Fr = np.cumsum(rest / rest.sum())
+    for w in np.linspace(0.001, 0.999, 53):
+        if np.min(np.abs(Fr - w)) < 1e-9:
+            continue
+        got = _run(vm, z[:2], onehot, [5], False, T, [0.999999], float(w))["committed"]
+        assert got == [int(np.searchsorted(Fr, w, side="right"))], (w, got)
+    # p(y) = 0 (token masked in the target): rejected even with u = 0
+    zm = z[:2].copy()
+    zm[0, 9] = -np.inf
+    r = _run(vm, zm, d[:1], [9], False, T, [0.0], 0.5)
+    assert r["a"] == 0 and r["committed"][0] != 9, r
+    # masked ids are never committed; zero-weight ids are never drawn, even at w = 0
+    zm = z.copy()
+    zm[:, :4] = -np.inf
+    for w in (0.0, 1e-9, 0.5):
+        r = _run(vm, zm[3:], d[:0], [], False, T, [], w)
+        assert r["committed"][0] >= 4, (w, r)
+    # a tiny temperature turns the bonus draw into the row argmax
+    zz = z[3].copy()
+    top = int(np.flatnonzero(zz == zz.max())[0])
+    zz[top] += 0.1                      # top gap >= 0.1: p(top) > 1 - 1e-40 at T = 1e-3
+    for w in (0.01, 0.5, 0.99):
+        r = _run(vm, zz[None, :], d[:0], [], False, 1e-3, [], w)
+        assert r["committed"] == [top], r
+    # the temperature matters: at T = 0.25 vs T = 4 the bonus differs for some w
+    outs = set()
+    for TT in (0.25, 4.0):
+        outs.add(tuple(_run(vm, z[:1], d[:0], [], False, TT, [], w)["committed"][0]
+                       for w in (0.1, 0.3, 0.5, 0.7, 0.9)))
+    assert len(outs) == 2
+
+
+def pin_greedy_invariants(vm, n_req: int = 300, V: int = 64, k: int = 4, seed: int = 5):
+    """On random rows with many exact ties: every kept draft attains its row's
+    maximum and no lower id does; the token at the cut attains the maximum with
+    no lower id doing so; a cut before k means the draft there was not that token."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n_req):
+        z = np.round(rng.normal(0, 1.0, size=(k + 1, V)) * 4) / 4   # coarse grid -> ties
+        m = z.max(axis=1)
+        ys = []
+        for i in range(k):
+            ids = np.flatnonzero(z[i] == m[i])
+            ys.append(int(ids[0]) if rng.random() < 0.6 else int(rng.integers(0, V)))
+        r = _run(vm, z, None, ys, True, None, [0.0] * k, 0.0)
+        a, c = r["a"], r["committed"]
+        assert len(c) == a + 1 and c[:a] == ys[:a]
+        for i in range(a + 1):
+            t = c[i]
+            assert z[i, t] == m[i] and not np.any(z[i, :t] == m[i]), (i, t)
+        if a < k:
+            assert ys[a] != c[a]
+
+
+def pin_cost_model():
+    """[CZ] section 2 illustration: 3 + 13 + 2 ms per round; A = 3 -> 4.5 ms/token,
+    A = 1 -> 9 ms/token, both below the 10 ms/token of ordinary decoding."""
+    from oracle.cost_model import time_per_token, expected_progress
+    assert time_per_token(3.0, 13.0, 2.0, 3.0) == 4.5
+    assert time_per_token(3.0, 13.0, 2.0, 1.0) == 9.0
+    assert time_per_token(3.0, 13.0, 2.0, 0.0) == 18.0
+    assert expected_progress([1.0, 1.0, 1.0], 3) == 4.0
+    assert expected_progress([0.5, 0.5], 2) == 1.75
+    assert expected_progress([0.9, 0.5, 0.2], 0) == 1.0
+
+
+def pin_packed_batch(vm):
+    """Ragged packing: requests of different k placed back to back give each
+    request's own fixture answer (offsets off[b] + b + i / off[b] + i)."""
+    g = load_golden("abr_example.json")
+    voc = {s: i for i, s in enumerate(g["vocab"])}
+    tgt = _logits_from_probs(g["target_probs"])
+    dr = _logits_from_probs(g["draft_probs"])
+    toks = [voc[s] for s in g["draft_tokens"]]
+    ks = [3, 0, 2, 4]
+    T_rows, D_rows, Y, U, W = [], [], [], [], []
+    for kk in ks:
+        T_rows.extend(tgt[:kk + 1])
+        D_rows.extend(dr[:kk])
+        Y.extend(toks[:kk])
+        U.extend([0.9, 0.9, 0.5, 0.1][:kk])
+        W.append(0.5)
+    res = vm.verify_batch(np.array(T_rows), np.array(D_rows).reshape(-1, 6), np.array(Y),
+                          np.array(ks), np.zeros(4, bool), 1.0, np.array(U, np.float32),
+                          np.array(W, np.float32))
+    R, A = voc["R"], voc["A"]
+    # k=3 (A B C, u_C = 0.5 >= 1/6 rejects) -> A B R;  k=0 -> bonus from p0 at w=.5
+    # (cumulative .40 .55 -> B);  k=2 -> A B + bonus from p2 at w=.5 (-> R);  k=4 -> A B R
+    assert list(res["accepted_len"]) == [2, 0, 2, 2], res["accepted_len"]
+    off = np.concatenate([[0], np.cumsum(ks)])
+    got = [list(res["out_tokens"][off[b] + b: off[b] + b + ks[b] + 1]) for b in range(4)]
+    assert got[0] == [A, voc["B"], R, -1], got
+    assert got[1] == [voc["B"]], got
+    assert got[2] == [A, voc["B"], R], got
+    assert got[3] == [A, voc["B"], R, -1, -1], got
+    assert np.all(res["resid_mass"][[0, 3]] > 0) and res["resid_mass"][1] == -1.0
+
+
+ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ties,
+            pin_exact_distribution_quadrature, pin_special_cases, pin_greedy_invariants,
+            pin_packed_batch]
