@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of one verification step on one MI355X.
+
+A step is one call of the C ABI (all kernels: plan, row statistics, decide,
+residual sweep, final draw) over one resident batch of synthetic logits.  The
+default workload is the ragged mixed batch (B=512, k_b uniform in 0..7,
+V=262144, bf16 logits, odd requests greedy, even requests stochastic at
+T=0.8), the only workload that exercises every step of the path.
+
+Prints ONE JSON line.  `value` = verified draft positions per second (sum of
+k_b per step / step time).  `roofline` describes the row-statistics kernel:
+algorithmic bytes (every logit row it must read, once) over its average
+duration measured with HIP events recorded around it on the call's stream.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (1× MI355X)"
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+SRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc", "spec_verify.hip")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime the process already uses."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b) -> float:
+        assert self.lib.hipEventSynchronize(b) == 0
+        ms = ctypes.c_float()
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def cpu_baseline(batch, min_seconds: float, max_requests: int):
+    """The oracle as it stands, on the first requests of the batch, until at
+    least `min_seconds` of CPU time have been spent (or `max_requests`)."""
+    import synth
+    import oracle
+    done_pos = 0
+    done_req = 0
+    rows = 0
+    t_total = 0.0
+    step = 16
+    while done_req < min(batch.B, max_requests) and t_total < min_seconds:
+        reqs = list(range(done_req, min(done_req + step, batch.B)))
+        sub = synth.select_requests(batch, reqs, device="cpu")
+        d = synth.as_numpy(sub)
+        t0 = time.perf_counter()
+        oracle.verify_batch(**d)
+        t_total += time.perf_counter() - t0
+        done_pos += int(sub.num_draft.sum())
+        rows += sub.K + sub.B + int(sub.num_draft[sub.greedy == 0].sum()) if sub.temperature else sub.K + sub.B
+        done_req += len(reqs)
+    return dict(value=done_pos / t_total if t_total > 0 else None, unit="verified draft positions/s",
+                cores=1, kind="oracle",
+                sample=f"first {done_req} of {batch.B} requests ({done_pos} positions, {rows} logit rows), "
+                       f"{t_total:.1f} s of fp64 NumPy on one host core")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup+steps calls and exit without the JSON report (for rocprofv3)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the verification step of a "
+                          "batch shards by request with no communication, so --gpus N > 1 is not "
+                          "measured here", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import draft_token_verification_row_amd as sv
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg_id = WORKLOADS[args.workload]
+    batch = synth.make_batch(cfg_id, dev)
+    torch.cuda.synchronize()
+
+    # Pre-built call: every buffer resident in HBM before timing.
+    nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=dev)
+    gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=dev) if batch.greedy.any() else None
+    acc = torch.empty(batch.B, dtype=torch.int32, device=dev)
+    out = torch.empty(batch.K + batch.B, dtype=torch.int32, device=dev)
+    pdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
+    qdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
+    rm = torch.empty(batch.B, dtype=torch.float32, device=dev)
+    ws_bytes = sv.spec_verify_workspace_bytes(batch.B, batch.K, batch.V)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    bt = sv.make_batch_struct(batch.target, batch.draft, batch.tokens, nd)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    lib = sv._lib
+    greedy_only = batch.temperature is None
+    if greedy_only:
+        def call():
+            return lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
+                                          ws.data_ptr(), ws_bytes, sh)
+    else:
+        T = ctypes.c_float(batch.temperature)
+        a_ptrs = (gm.data_ptr() if gm is not None else None, batch.u_accept.data_ptr(),
+                  batch.u_final.data_ptr(), acc.data_ptr(), out.data_ptr(), pdr.data_ptr(),
+                  qdr.data_ptr(), rm.data_ptr())
+
+        def call():
+            return lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes, sh)
+
+    for _ in range(args.warmup):
+        assert call() == 0
+    torch.cuda.synchronize()
+    if args.profile_only:
+        for _ in range(args.steps):
+            assert call() == 0
+        torch.cuda.synchronize()
+        print(f"profile-only: {args.warmup + args.steps} calls of {batch.name}", flush=True)
+        return
+
+    hip = HipEvents()
+    ev_b = hip.create(args.steps)
+    ev_e = hip.create(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+        call()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sv.spec_verify_set_profile_events(None, None)
+    stats_ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(args.steps)]
+    hip.destroy(ev_b + ev_e)
+
+    step_s = (t1 - t0) / args.steps
+    positions = int(batch.num_draft.sum())
+    es = 4 if batch.dtype == "f32" else 2
+    stoch_draft_rows = 0 if greedy_only else int(batch.num_draft[batch.greedy == 0].sum())
+    rows = batch.K + batch.B + stoch_draft_rows
+    bytes_stats = rows * batch.V * es                 # every row the kernel must read, once
+    t_stats = float(np.mean(stats_ms)) / 1e3
+    achieved = bytes_stats / t_stats / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC):
+        with open(TRAFFIC) as f:
+            tr = json.load(f)
+        entry = tr.get(batch.name)
+        if entry and entry.get("source_hash") == kernel_source_hash():
+            traffic = entry.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": positions / step_s,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": batch.name, "B": batch.B, "K": batch.K, "V": batch.V,
+            "logits": batch.dtype, "temperature": batch.temperature,
+            "requests": ("greedy" if greedy_only else
+                         f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
+            "parallelism": "single GPU",
+        },
+        "rows_per_s": (batch.K + batch.B) / step_s,
+        "hbm_gbs_step": bytes_stats / step_s / 1e9,
+        "hbm_frac_step": bytes_stats / step_s / 1e9 / PEAK_HBM_GBS,
+        "roofline": {
+            "kernel": "k_stats (row statistics)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": bytes_stats,
+            "avg_kernel_ms": t_stats * 1e3,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, max_requests=batch.B)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

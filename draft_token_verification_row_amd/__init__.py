@@ -1,0 +1,188 @@
+"""Python binding of libspecverify.so (one-round draft-token verification, gfx950).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels behind the C ABI of include/spec_verify.h.  PyTorch supplies device
+memory and the current stream.  The functions carry the C names.
+
+If the library has not been built, importing this package raises ImportError:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_UNSUPPORTED, SV_ERR_WORKSPACE, SV_ERR_HIP = range(5)
+SV_F32, SV_BF16 = 0, 1
+_DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
+
+# Every function the C header declares (checked by the CPU test suite).
+EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
+            "spec_verify_greedy", "spec_verify_sample", "spec_verify_set_profile_events")
+
+
+class SvBatch(ctypes.Structure):
+    """Mirror of sv_batch_t."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("K", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("target_ld", ctypes.c_int64), ("draft_ld", ctypes.c_int64),
+        ("num_draft", ctypes.c_void_p), ("target", ctypes.c_void_p),
+        ("draft", ctypes.c_void_p), ("draft_tokens", ctypes.c_void_p),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify_status_string.argtypes = [i32]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_greedy.argtypes = [ctypes.POINTER(SvBatch), vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.restype = i32
+    lib.spec_verify_sample.argtypes = [ctypes.POINTER(SvBatch), ctypes.c_float, vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_sample.restype = i32
+    lib.spec_verify_set_profile_events.argtypes = [vp, vp]
+    lib.spec_verify_set_profile_events.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"spec_verify status {status}: {spec_verify_status_string(status)}")
+        self.status = status
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} dtype {t.dtype} unsupported (float32 or bfloat16)")
+    return t.stride(0)
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def spec_verify_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(_lib.spec_verify_workspace_bytes(B, K, V))
+
+
+def spec_verify_status_string(status: int) -> str:
+    return _lib.spec_verify_status_string(status).decode()
+
+
+def spec_verify_set_profile_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
+    return int(_lib.spec_verify_set_profile_events(ev_begin, ev_end))
+
+
+def make_batch_struct(target: torch.Tensor, draft: Optional[torch.Tensor],
+                      draft_tokens: torch.Tensor, num_draft: torch.Tensor) -> SvBatch:
+    tld = _rows(target, "target")
+    dld = 0
+    if draft is not None:
+        dld = _rows(draft, "draft")
+        if draft.dtype != target.dtype:
+            raise ValueError("target and draft logits must share a dtype")
+    B = int(num_draft.numel())
+    K = int(draft_tokens.numel())
+    return SvBatch(B=B, K=K, V=int(target.shape[1]), dtype=_DTYPES[target.dtype],
+                   target_ld=tld, draft_ld=dld, num_draft=_ptr(num_draft), target=_ptr(target),
+                   draft=_ptr(draft), draft_tokens=_ptr(draft_tokens) if K > 0 else None)
+
+
+def _workspace(B, K, V, workspace, device):
+    need = spec_verify_workspace_bytes(B, K, V)
+    if need == 0:
+        raise SpecVerifyError(SV_ERR_INVALID_ARG)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, num_draft: torch.Tensor,
+                       *, accepted_len=None, out_tokens=None, workspace=None, stream=None):
+    """Greedy verification; returns (accepted_len [B], out_tokens [K+B]) int32 tensors."""
+    bt = make_batch_struct(target, None, draft_tokens, num_draft)
+    dev = target.device
+    if accepted_len is None:
+        accepted_len = torch.empty(bt.B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(bt.K + bt.B, dtype=torch.int32, device=dev)
+    workspace, wsb = _workspace(bt.B, bt.K, bt.V, workspace, dev)
+    st = _lib.spec_verify_greedy(ctypes.byref(bt), _ptr(accepted_len), _ptr(out_tokens),
+                                 _ptr(workspace), wsb, _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accepted_len, out_tokens
+
+
+def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
+                       draft_tokens: torch.Tensor, num_draft: torch.Tensor, temperature: float,
+                       u_accept: torch.Tensor, u_final: torch.Tensor, *, greedy_mask=None,
+                       accepted_len=None, out_tokens=None, p_draft=None, q_draft=None,
+                       resid_mass=None, want_probs: bool = True, workspace=None, stream=None):
+    """Stochastic (optionally mixed greedy) verification.
+
+    Returns a dict of device tensors: accepted_len, out_tokens, p_draft, q_draft,
+    resid_mass (the last three None when want_probs is False and none was given).
+    """
+    bt = make_batch_struct(target, draft, draft_tokens, num_draft)
+    dev = target.device
+    if accepted_len is None:
+        accepted_len = torch.empty(bt.B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(bt.K + bt.B, dtype=torch.int32, device=dev)
+    if want_probs:
+        if p_draft is None:
+            p_draft = torch.empty(bt.K, dtype=torch.float32, device=dev)
+        if q_draft is None:
+            q_draft = torch.empty(bt.K, dtype=torch.float32, device=dev)
+        if resid_mass is None:
+            resid_mass = torch.empty(bt.B, dtype=torch.float32, device=dev)
+    workspace, wsb = _workspace(bt.B, bt.K, bt.V, workspace, dev)
+    st = _lib.spec_verify_sample(
+        ctypes.byref(bt), ctypes.c_float(temperature), _ptr(greedy_mask), _ptr(u_accept),
+        _ptr(u_final), _ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+        _ptr(resid_mass), _ptr(workspace), wsb, _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,
+                q_draft=q_draft, resid_mass=resid_mass)
+
+
+def verify_batch(batch, *, workspace=None, want_probs=True, stream=None):
+    """Run a synthetic batch object (fields as produced by the input generator)."""
+    nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=batch.target.device)
+    if batch.temperature is None:
+        acc, out = spec_verify_greedy(batch.target, batch.tokens, nd, workspace=workspace,
+                                      stream=stream)
+        return dict(accepted_len=acc, out_tokens=out, p_draft=None, q_draft=None,
+                    resid_mass=None)
+    gm = None
+    if batch.greedy.any():
+        gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=batch.target.device)
+    return spec_verify_sample(batch.target, batch.draft, batch.tokens, nd, batch.temperature,
+                              batch.u_accept, batch.u_final, greedy_mask=gm,
+                              want_probs=want_probs, workspace=workspace, stream=stream)

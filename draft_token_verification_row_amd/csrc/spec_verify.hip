@@ -1,0 +1,1057 @@
+// spec_verify.hip - one-round draft-token verification for AMD Instinct MI355X (gfx950).
+//
+// Implements the C ABI of include/spec_verify.h.  The operation is the
+// verification step of one speculative-decoding round (chzhyang, "Speculative
+// Decoding: Medusa, MTP, EAGLE, DFlash, DDTree, and DSpark", section 1; vLLM blog
+// "speculative-decoding-amd-gpus", "Core idea of speculative decoding").
+//
+// Pipeline (all launches on the caller's stream, no host synchronisation):
+//   k_plan      one workgroup: exclusive scan of num_draft -> request offsets,
+//               compact list of logit rows to read (every target row, the draft
+//               rows of stochastic requests), unit count.
+//   k_stats     persistent grid, one wavefront per 32 KiB slice ("unit") of a
+//               row.  Streams the logits once from HBM with 16-byte loads and
+//               writes per-unit partials: online max and sum of exp((z-max)/T)
+//               for softmax rows, (max, lowest id) for greedy rows.  This is the
+//               HBM-bound kernel that carries almost all bytes.
+//   k_decide    one wavefront per request: combines the partials of each row,
+//               evaluates p(y_i), q(y_i) in fp64, runs the ratio test (stochastic)
+//               or argmax test (greedy) for every position, cuts at the first
+//               rejection, commits the kept drafts and the greedy target token,
+//               and queues a residual job for stochastic requests cut early.
+//   k_resid     persistent grid: second sweep of the one (target, draft) row pair
+//               of each queued request, per-unit sums of [p - q]_+.
+//   k_finalize  one workgroup per stochastic request: finds the unit holding
+//               the inverse-CDF crossing from the unit sums (bonus: from the
+//               k_stats partials, no re-read), rescans that unit only and writes
+//               the correction / bonus token.
+//
+// Numerics.  exp((z - m)/T) is evaluated as exp2((z - m) * c) with
+// c = log2(e)/T split into two fp32 constants (c_hi + c_lo), so the rounding of
+// c does not bias whole rows.  Lane partial sums are fp32 over at most a few
+// dozen terms, combined across lanes, units and rows in fp64.  p(y) and q(y)
+// are formed in fp64 from the exact logit at y.  Greedy argmax is exact
+// (lexicographic max of (value, -id)).
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "spec_verify.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kUnroll = 8;           // 16-byte loads in flight per lane per row
+constexpr int kSegBytes = 32768;     // one unit = 32 KiB of one logit row
+constexpr int kSegMinElems = kSegBytes / 4;
+constexpr int kBlocksPerCU = 8;      // 32 wavefronts per CU
+constexpr int kPlanThreads = 1024;
+
+constexpr uint32_t kDraftBit = 1u << 30;
+constexpr uint32_t kGreedyBit = 1u << 29;
+constexpr uint32_t kRowMask = kGreedyBit - 1u;
+
+enum Kind : int { KIND_NONE = 0, KIND_RESID = 1, KIND_BONUS = 2, KIND_INVALID = 3 };
+enum DrawMode : int { DRAW_RESID = 0, DRAW_FROM_P = 1 };
+
+struct Partial {      // one unit of one row
+  double s;           // sum of exp2((z - m) * c) over the unit (softmax rows)
+  float m;            // max logit of the unit
+  int idx;            // lowest id attaining m (greedy rows)
+};
+
+struct ReqInfo {      // per request; plan fills off/k/greedy, decide the rest
+  int off, k, greedy, a;
+  int kind, y, trow, drow;
+  float Mp, Mq;
+  int pad0, pad1;
+  double Sp, Sq;
+};
+
+struct Header {
+  int error;
+  int n_rows;
+  int n_units;
+  int n_resid;
+  int pad[60];
+};
+
+struct Workspace {
+  Header* hdr;
+  ReqInfo* req;
+  uint32_t* rowdesc;   // [2K + B]
+  int* resid_list;     // [B]
+  Partial* pt;         // [(K + B) * nseg]
+  Partial* pd;         // [K * nseg]
+  double* rp;          // [B * nseg]
+};
+
+struct Args {
+  int B, K, V, nseg, seg;
+  int force_greedy;
+  int64_t tld, dld;
+  const void* target;
+  const void* draft;
+  const int* num_draft;
+  const int* tokens;
+  const uint8_t* gmask;
+  const float* u_accept;
+  const float* u_final;
+  int* acc_len;
+  int* out;
+  float* p_out;
+  float* q_out;
+  float* resid_out;
+  float c_hi, c_lo;    // log2(e)/T split into two fp32 constants, c_lo > 0
+  double c64, T64;
+  Workspace ws;
+};
+
+// ------------------------------------------------------------------ element access
+struct F32 {
+  using Elem = float;
+  static constexpr int E = 4;
+  using Raw = float4;
+  __device__ static __forceinline__ Raw load(const Elem* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+  __device__ static __forceinline__ float one(const Elem* p) { return *p; }
+};
+
+struct BF16 {
+  using Elem = uint16_t;
+  static constexpr int E = 8;
+  using Raw = uint4;
+  __device__ static __forceinline__ Raw load(const Elem* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
+    v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xffff0000u);
+    v[4] = __uint_as_float(r.z << 16); v[5] = __uint_as_float(r.z & 0xffff0000u);
+    v[6] = __uint_as_float(r.w << 16); v[7] = __uint_as_float(r.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ float one(const Elem* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+};
+
+// Unaligned rows: one element per "chunk", plain scalar loads.
+template <class D>
+struct Scalar {
+  using Elem = typename D::Elem;
+  static constexpr int E = 1;
+  using Raw = float;
+  __device__ static __forceinline__ Raw load(const Elem* p) { return D::one(p); }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) { v[0] = r; }
+  __device__ static __forceinline__ float one(const Elem* p) { return D::one(p); }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp((z - m)/T) = exp2(d * c) with d = z - m and c = c_hi + c_lo.
+__device__ __forceinline__ float scaled_exp(float d, float c_hi, float c_lo) {
+  return fast_exp2(fmaf(d, c_hi, d * c_lo));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Visit the unit [s0, s1) of one row, chunk by chunk, in increasing id order
+// per lane.  f(v, first_id, count) receives E values (padding = -inf).
+template <class L, class F>
+__device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, int s1,
+                                         int lane, F& f) {
+  constexpr int E = L::E;
+  const int n = s1 - s0;
+  const int nchunk = n / E;
+  const typename L::Elem* p = row + s0;
+  constexpr int per_it = kWave * kUnroll;
+  const int nit = nchunk / per_it;
+  int c = lane;
+  for (int it = 0; it < nit; ++it, c += per_it) {
+    typename L::Raw r[kUnroll];
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) r[j] = L::load(p + (size_t)(c + j * kWave) * E);
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      float v[E];
+      L::unpack(r[j], v);
+      f(v, s0 + (c + j * kWave) * E, E);
+    }
+  }
+  for (; c < nchunk; c += kWave) {
+    float v[E];
+    L::unpack(L::load(p + (size_t)c * E), v);
+    f(v, s0 + c * E, E);
+  }
+  const int tail0 = nchunk * E;
+  if (lane < n - tail0) {
+    float v[E];
+    v[0] = L::one(p + tail0 + lane);
+#pragma unroll
+    for (int e = 1; e < E; ++e) v[e] = -INFINITY;
+    f(v, s0 + tail0 + lane, 1);
+  }
+}
+
+template <int E>
+struct SoftmaxAcc {
+  float m;
+  float s[E];
+  float c_hi, c_lo;
+  __device__ __forceinline__ void operator()(const float* v, int, int) {
+    float cm = v[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
+    if (cm > m) {                    // rare after the first chunks
+      const float f = scaled_exp(m - cm, c_hi, c_lo);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] *= f;
+      m = cm;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] += scaled_exp(v[e] - m, c_hi, c_lo);
+  }
+};
+
+template <int E>
+struct ArgmaxAcc {
+  float best;
+  int idx;
+  __device__ __forceinline__ void operator()(const float* v, int id0, int cnt) {
+    float cm = v[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
+    if (cm > best) {                 // ids only grow within a lane: strict > keeps the lowest
+      int hit = 0;
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e)
+        if (v[e] == cm) hit = e;
+      if (hit < cnt) {
+        best = cm;
+        idx = id0 + hit;
+      }
+    }
+  }
+};
+
+template <class L>
+__device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
+                             const Args& a, Partial* out) {
+  SoftmaxAcc<L::E> acc;
+  acc.m = -FLT_MAX;
+  acc.c_hi = a.c_hi;
+  acc.c_lo = a.c_lo;
+#pragma unroll
+  for (int e = 0; e < L::E; ++e) acc.s[e] = 0.f;
+  for_unit<L>(row, s0, s1, lane, acc);
+  float sl = 0.f;
+#pragma unroll
+  for (int e = 0; e < L::E; ++e) sl += acc.s[e];
+  const float mw = wave_max(acc.m);
+  const double f = exp2(((double)acc.m - (double)mw) * a.c64);
+  const double sw = wave_sum((double)sl * f);
+  if (lane == 0) {
+    Partial p;
+    p.s = sw;
+    p.m = mw;
+    p.idx = 0;
+    *out = p;
+  }
+}
+
+template <class L>
+__device__ void argmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
+                            Partial* out) {
+  ArgmaxAcc<L::E> acc;
+  acc.best = -INFINITY;
+  acc.idx = INT_MAX;
+  for_unit<L>(row, s0, s1, lane, acc);
+  float b = acc.best;
+  int i = acc.idx;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(b, o);
+    const int oi = __shfl_xor(i, o);
+    if (ob > b || (ob == b && oi < i)) {
+      b = ob;
+      i = oi;
+    }
+  }
+  if (lane == 0) {
+    Partial p;
+    p.s = 0.0;
+    p.m = b;
+    p.idx = i;
+    *out = p;
+  }
+}
+
+// ------------------------------------------------------------------ k_plan
+__global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
+  __shared__ long long sk[kPlanThreads];
+  __shared__ long long ss[kPlanThreads];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const long long TB = (long long)a.K + a.B;
+  long long carry_k = 0, carry_s = 0;
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int b = base + tid;
+    long long k = 0;
+    int g = 1;
+    if (b < a.B) {
+      int kk = a.num_draft[b];
+      if (kk < 0 || kk > a.K) {
+        s_bad = 1;
+        kk = 0;
+      }
+      k = kk;
+      g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
+    }
+    const long long ks = g ? 0 : k;
+    sk[tid] = k;
+    ss[tid] = ks;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {
+      const long long xk = tid >= o ? sk[tid - o] : 0;
+      const long long xs = tid >= o ? ss[tid - o] : 0;
+      __syncthreads();
+      sk[tid] += xk;
+      ss[tid] += xs;
+      __syncthreads();
+    }
+    const long long off = carry_k + sk[tid] - k;
+    const long long soff = carry_s + ss[tid] - ks;
+    const long long tot_k = sk[kPlanThreads - 1];
+    const long long tot_s = ss[kPlanThreads - 1];
+    if (b < a.B) {
+      ReqInfo r;
+      r.off = (int)off;
+      r.k = (int)k;
+      r.greedy = g;
+      r.a = 0;
+      r.kind = KIND_NONE;
+      r.y = -1;
+      r.trow = -1;
+      r.drow = -1;
+      r.Mp = r.Mq = 0.f;
+      r.pad0 = r.pad1 = 0;
+      r.Sp = r.Sq = 0.0;
+      a.ws.req[b] = r;
+      for (long long i = 0; i <= k; ++i) {
+        const long long row = off + b + i;
+        if (row < TB) a.ws.rowdesc[row] = (uint32_t)row | (g ? kGreedyBit : 0u);
+      }
+      if (!g) {
+        for (long long i = 0; i < k; ++i) {
+          const long long slot = TB + soff + i;
+          if (slot < TB + a.K) a.ws.rowdesc[slot] = (uint32_t)(off + i) | kDraftBit;
+        }
+      }
+    }
+    carry_k += tot_k;
+    carry_s += tot_s;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const bool bad = s_bad != 0 || carry_k != a.K;
+    const long long nrows = bad ? 0 : TB + carry_s;
+    Header* h = a.ws.hdr;
+    h->error = bad ? 1 : 0;
+    h->n_rows = (int)nrows;
+    h->n_units = (int)(nrows * a.nseg);
+    h->n_resid = 0;
+  }
+}
+
+// ------------------------------------------------------------------ k_stats
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_stats(Args a) {
+  using Elem = typename L::Elem;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int W = gridDim.x * kWavesPerBlock;
+  const int n_units = a.ws.hdr->n_units;
+  const Elem* tgt = static_cast<const Elem*>(a.target);
+  const Elem* drf = static_cast<const Elem*>(a.draft);
+  for (int u = gw; u < n_units; u += W) {
+    const int ri = u / a.nseg;
+    const int seg = u - ri * a.nseg;
+    const uint32_t desc = a.ws.rowdesc[ri];
+    const int row = (int)(desc & kRowMask);
+    const bool is_draft = (desc & kDraftBit) != 0;
+    const bool greedy = (desc & kGreedyBit) != 0;
+    const int s0 = seg * a.seg;
+    const int s1 = min(s0 + a.seg, a.V);
+    const Elem* base = is_draft ? drf + (int64_t)row * a.dld : tgt + (int64_t)row * a.tld;
+    Partial* out = (is_draft ? a.ws.pd : a.ws.pt) + (int64_t)row * a.nseg + seg;
+    if (greedy)
+      argmax_unit<L>(base, s0, s1, lane, out);
+    else
+      softmax_unit<L>(base, s0, s1, lane, a, out);
+  }
+}
+
+// ------------------------------------------------------------------ row combines
+__device__ void combine_softmax(const Partial* P, int nseg, double T64, float& M, double& S) {
+  float m = -FLT_MAX;
+  for (int s = 0; s < nseg; ++s) m = fmaxf(m, P[s].m);
+  double acc = 0.0;
+  for (int s = 0; s < nseg; ++s) {
+    const Partial p = P[s];
+    if (p.s > 0.0) acc += p.s * exp(((double)p.m - (double)m) / T64);
+  }
+  M = m;
+  S = acc;
+}
+
+__device__ void combine_argmax(const Partial* P, int nseg, int& idx) {
+  float bm = -INFINITY;
+  int bi = INT_MAX;
+  for (int s = 0; s < nseg; ++s) {
+    const Partial p = P[s];
+    if (p.m > bm || (p.m == bm && p.idx < bi)) {
+      bm = p.m;
+      bi = p.idx;
+    }
+  }
+  idx = bi;
+}
+
+template <class D>
+__device__ __forceinline__ float logit_at(const void* base, int64_t row, int64_t ld, int v) {
+  return D::one(static_cast<const typename D::Elem*>(base) + row * ld + v);
+}
+
+// ------------------------------------------------------------------ k_decide
+template <class D>
+__global__ __launch_bounds__(kBlock) void k_decide(Args a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (a.ws.hdr->error) {
+    // inconsistent num_draft: every output slot becomes -1
+    const long long gt = (long long)blockIdx.x * kBlock + threadIdx.x;
+    const long long gs = (long long)gridDim.x * kBlock;
+    for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
+    for (long long i = gt; i < a.B; i += gs) {
+      a.acc_len[i] = -1;
+      if (a.resid_out) a.resid_out[i] = -1.f;
+    }
+    for (long long i = gt; i < a.K; i += gs) {
+      if (a.p_out) a.p_out[i] = -1.f;
+      if (a.q_out) a.q_out[i] = -1.f;
+    }
+    return;
+  }
+  if (b >= a.B) return;
+  const ReqInfo R = a.ws.req[b];
+  const int k = R.k;
+  const int trow0 = R.off + b;
+  const int drow0 = R.off;
+  const bool g = R.greedy != 0;
+  const int nseg = a.nseg;
+  int first_rej = k;
+  bool invalid = false;
+  for (int base = 0; base < k; base += kWave) {
+    const int i = base + lane;
+    bool rej = false;
+    if (i < k) {
+      const int y = a.tokens[drow0 + i];
+      if (g) {
+        int idx;
+        combine_argmax(a.ws.pt + (int64_t)(trow0 + i) * nseg, nseg, idx);
+        rej = (y != idx);
+      } else if (y < 0 || y >= a.V) {
+        invalid = true;
+        if (a.p_out) a.p_out[drow0 + i] = -1.f;
+        if (a.q_out) a.q_out[drow0 + i] = -1.f;
+      } else {
+        float Mp, Mq;
+        double Sp, Sq;
+        combine_softmax(a.ws.pt + (int64_t)(trow0 + i) * nseg, nseg, a.T64, Mp, Sp);
+        combine_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.T64, Mq, Sq);
+        const float zy = logit_at<D>(a.target, trow0 + i, a.tld, y);
+        const float dy = logit_at<D>(a.draft, drow0 + i, a.dld, y);
+        const double py = exp(((double)zy - (double)Mp) / a.T64) / Sp;
+        const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
+        rej = !((double)a.u_accept[drow0 + i] * qy < py);
+        if (a.p_out) a.p_out[drow0 + i] = (float)py;
+        if (a.q_out) a.q_out[drow0 + i] = (float)qy;
+      }
+    }
+    const unsigned long long rm = __ballot(rej);
+    if (rm != 0ull && first_rej == k) first_rej = base + __ffsll((long long)rm) - 1;
+    if (g && first_rej < k) break;
+  }
+  if (__any(invalid)) {
+    for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
+    if (lane == 0) {
+      a.acc_len[b] = -1;
+      if (a.resid_out) a.resid_out[b] = -1.f;
+      a.ws.req[b].kind = KIND_INVALID;
+    }
+    return;
+  }
+  const int A = first_rej;
+  int final_tok = -1;
+  if (g) {
+    for (int i = lane; i < k; i += kWave) {   // no probabilities for greedy rows
+      if (a.p_out) a.p_out[drow0 + i] = -1.f;
+      if (a.q_out) a.q_out[drow0 + i] = -1.f;
+    }
+    int idx = INT_MAX;
+    if (lane == 0) combine_argmax(a.ws.pt + (int64_t)(trow0 + A) * nseg, nseg, idx);
+    idx = __shfl(idx, 0);
+    final_tok = (idx == INT_MAX) ? -1 : idx;
+  }
+  for (int i = lane; i <= k; i += kWave) {
+    int v = -1;
+    if (i < A) v = a.tokens[drow0 + i];
+    else if (i == A) v = final_tok;     // stochastic: written by k_finalize
+    a.out[trow0 + i] = v;
+  }
+  if (lane == 0) {
+    a.acc_len[b] = A;
+    if (a.resid_out) a.resid_out[b] = -1.f;
+    ReqInfo W = R;
+    W.a = A;
+    W.trow = trow0 + A;
+    if (g) {
+      W.kind = KIND_NONE;
+    } else {
+      combine_softmax(a.ws.pt + (int64_t)(trow0 + A) * nseg, nseg, a.T64, W.Mp, W.Sp);
+      if (A < k) {
+        W.kind = KIND_RESID;
+        W.drow = drow0 + A;
+        W.y = a.tokens[drow0 + A];
+        combine_softmax(a.ws.pd + (int64_t)(drow0 + A) * nseg, nseg, a.T64, W.Mq, W.Sq);
+        const int j = atomicAdd(&a.ws.hdr->n_resid, 1);
+        a.ws.resid_list[j] = b;
+      } else {
+        W.kind = KIND_BONUS;
+        W.drow = -1;
+        W.y = -1;
+      }
+    }
+    a.ws.req[b] = W;
+  }
+}
+
+// ------------------------------------------------------------------ residual weights
+struct ResidW {
+  float Mp, Mq, ip, iq, c_hi, c_lo;
+  __device__ __forceinline__ float operator()(float z, float d) const {
+    const float p = scaled_exp(z - Mp, c_hi, c_lo) * ip;
+    const float q = scaled_exp(d - Mq, c_hi, c_lo) * iq;
+    return fmaxf(p - q, 0.f);
+  }
+};
+
+struct TargetW {
+  float Mp, ip, c_hi, c_lo;
+  __device__ __forceinline__ float operator()(float z) const {
+    return scaled_exp(z - Mp, c_hi, c_lo) * ip;
+  }
+};
+
+// ------------------------------------------------------------------ k_resid
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_resid(Args a) {
+  using Elem = typename L::Elem;
+  constexpr int E = L::E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int W = gridDim.x * kWavesPerBlock;
+  const int n_units = a.ws.hdr->n_resid * a.nseg;
+  for (int u = gw; u < n_units; u += W) {
+    const int j = u / a.nseg;
+    const int seg = u - j * a.nseg;
+    const int b = a.ws.resid_list[j];
+    const ReqInfo R = a.ws.req[b];
+    ResidW fw;
+    fw.Mp = R.Mp;
+    fw.Mq = R.Mq;
+    fw.ip = (float)(1.0 / R.Sp);
+    fw.iq = (float)(1.0 / R.Sq);
+    fw.c_hi = a.c_hi;
+    fw.c_lo = a.c_lo;
+    const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
+    const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
+    const int s0 = seg * a.seg;
+    const int s1 = min(s0 + a.seg, a.V);
+    const int n = s1 - s0;
+    const int nchunk = n / E;
+    const int y = R.y;
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    constexpr int U = kUnroll / 2;
+    constexpr int per_it = kWave * U;
+    const int nit = nchunk / per_it;
+    int c = lane;
+    auto chunk = [&](const typename L::Raw& rt, const typename L::Raw& rd, int id0) {
+      float vt[E], vd[E];
+      L::unpack(rt, vt);
+      L::unpack(rd, vd);
+      float r[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) r[e] = fw(vt[e], vd[e]);
+      if ((unsigned)(y - id0) < (unsigned)E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (id0 + e == y) r[e] = 0.f;   // reject => p(y) < q(y) => [p - q]_+ is 0 at y
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += r[e];
+    };
+    for (int it = 0; it < nit; ++it, c += per_it) {
+      typename L::Raw rt[U], rd[U];
+#pragma unroll
+      for (int jj = 0; jj < U; ++jj) {
+        rt[jj] = L::load(tp + s0 + (size_t)(c + jj * kWave) * E);
+        rd[jj] = L::load(dp + s0 + (size_t)(c + jj * kWave) * E);
+      }
+#pragma unroll
+      for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
+    }
+    for (; c < nchunk; c += kWave)
+      chunk(L::load(tp + s0 + (size_t)c * E), L::load(dp + s0 + (size_t)c * E), s0 + c * E);
+    const int tail0 = nchunk * E;
+    if (lane < n - tail0) {
+      const int v = s0 + tail0 + lane;
+      if (v != y) acc[0] += fw(L::one(tp + v), L::one(dp + v));
+    }
+    float sl = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) sl += acc[e];
+    const double tot = wave_sum((double)sl);
+    if (lane == 0) a.ws.rp[(int64_t)b * a.nseg + seg] = tot;
+  }
+}
+
+// ------------------------------------------------------------------ k_finalize
+template <class L>
+__device__ __forceinline__ double range_sum_resid(const typename L::Elem* tp,
+                                                  const typename L::Elem* dp, int v0, int v1,
+                                                  const ResidW& fw, int y) {
+  constexpr int E = L::E;
+  double s = 0.0;
+  int v = v0;
+  for (; v + E <= v1; v += E) {
+    float vt[E], vd[E];
+    L::unpack(L::load(tp + v), vt);
+    L::unpack(L::load(dp + v), vd);
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs += (v + e == y) ? 0.f : fw(vt[e], vd[e]);
+    s += (double)cs;
+  }
+  for (; v < v1; ++v) s += (v == y) ? 0.0 : (double)fw(L::one(tp + v), L::one(dp + v));
+  return s;
+}
+
+template <class L>
+__device__ __forceinline__ double range_sum_target(const typename L::Elem* tp, int v0, int v1,
+                                                   const TargetW& fw) {
+  constexpr int E = L::E;
+  double s = 0.0;
+  int v = v0;
+  for (; v + E <= v1; v += E) {
+    float vt[E];
+    L::unpack(L::load(tp + v), vt);
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cs += fw(vt[e]);
+    s += (double)cs;
+  }
+  for (; v < v1; ++v) s += (double)fw(L::one(tp + v));
+  return s;
+}
+
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
+  using Elem = typename L::Elem;
+  constexpr int E = L::E;
+  __shared__ double s_part[kBlock];
+  __shared__ double s_thr, s_base, s_Z;
+  __shared__ int s_seg, s_mode, s_j, s_fallback;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  if (a.ws.hdr->error) return;
+  const ReqInfo R = a.ws.req[b];
+  if (R.kind != KIND_RESID && R.kind != KIND_BONUS) return;
+  const int nseg = a.nseg;
+  const Partial* prow = a.ws.pt + (int64_t)R.trow * nseg;
+  if (tid == 0) {
+    int mode = (R.kind == KIND_RESID) ? DRAW_RESID : DRAW_FROM_P;
+    double Z = 0.0;
+    if (mode == DRAW_RESID) {
+      for (int s = 0; s < nseg; ++s) Z += a.ws.rp[(int64_t)b * nseg + s];
+      if (!(Z > 0.0)) mode = DRAW_FROM_P;      // p == q numerically: draw from p
+    }
+    if (mode == DRAW_FROM_P) {
+      Z = 0.0;
+      for (int s = 0; s < nseg; ++s) {
+        const Partial p = prow[s];
+        if (p.s > 0.0) Z += p.s * exp(((double)p.m - (double)R.Mp) / a.T64) / R.Sp;
+      }
+    }
+    const double thr = (double)a.u_final[b] * Z;
+    double cum = 0.0;
+    int seg = -1, last_pos = -1;
+    double cum_last = 0.0;
+    for (int s = 0; s < nseg; ++s) {
+      double m;
+      if (mode == DRAW_RESID) {
+        m = a.ws.rp[(int64_t)b * nseg + s];
+      } else {
+        const Partial p = prow[s];
+        m = (p.s > 0.0) ? p.s * exp(((double)p.m - (double)R.Mp) / a.T64) / R.Sp : 0.0;
+      }
+      if (cum + m > thr) {
+        seg = s;
+        break;
+      }
+      if (m > 0.0) {
+        last_pos = s;
+        cum_last = cum;
+      }
+      cum += m;
+    }
+    s_fallback = 0;
+    if (seg < 0) {               // rounding left w*Z at or past the end
+      seg = last_pos < 0 ? 0 : last_pos;
+      cum = cum_last;
+      s_fallback = 1;
+    }
+    s_seg = seg;
+    s_base = cum;
+    s_thr = thr;
+    s_mode = mode;
+    s_Z = Z;
+  }
+  __syncthreads();
+  const int seg = s_seg;
+  const int mode = s_mode;
+  const double thr = s_thr;
+  const int s0 = seg * a.seg;
+  const int s1 = min(s0 + a.seg, a.V);
+  const int n = s1 - s0;
+  int L_ = (n + kBlock - 1) / kBlock;
+  L_ = (L_ + E - 1) / E * E;
+  const int v0 = min(s0 + tid * L_, s1);
+  const int v1 = min(v0 + L_, s1);
+  const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
+  const Elem* dp = (R.drow >= 0) ? static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld
+                                 : nullptr;
+  ResidW rw;
+  rw.Mp = R.Mp; rw.Mq = R.Mq;
+  rw.ip = (float)(1.0 / R.Sp);
+  rw.iq = (float)(1.0 / R.Sq);
+  rw.c_hi = a.c_hi; rw.c_lo = a.c_lo;
+  TargetW tw;
+  tw.Mp = R.Mp;
+  tw.ip = (float)(1.0 / R.Sp);
+  tw.c_hi = a.c_hi; tw.c_lo = a.c_lo;
+  const double mine = (mode == DRAW_RESID) ? range_sum_resid<L>(tp, dp, v0, v1, rw, R.y)
+                                           : range_sum_target<L>(tp, v0, v1, tw);
+  s_part[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {
+    double cum = s_base;
+    int j = -1, last = -1;
+    double cum_last = s_base;
+    if (!s_fallback) {
+      for (int t = 0; t < kBlock; ++t) {
+        if (cum + s_part[t] > thr) {
+          j = t;
+          break;
+        }
+        if (s_part[t] > 0.0) {
+          last = t;
+          cum_last = cum;
+        }
+        cum += s_part[t];
+      }
+    } else {
+      for (int t = 0; t < kBlock; ++t) {
+        if (s_part[t] > 0.0) {
+          last = t;
+          cum_last = cum;
+        }
+        cum += s_part[t];
+      }
+    }
+    int fb = s_fallback;
+    if (j < 0) {
+      j = last;
+      cum = cum_last;
+      fb = 1;
+    }
+    s_j = j;
+    s_base = cum;
+    s_fallback = fb;
+  }
+  __syncthreads();
+  if (tid == s_j) {
+    // walk this thread's ids in ascending order
+    double cum = s_base;
+    int tok = -1, last_pos = -1;
+    for (int v = v0; v < v1; ++v) {
+      float wv;
+      if (mode == DRAW_RESID)
+        wv = (v == R.y) ? 0.f : rw(L::one(tp + v), L::one(dp + v));
+      else
+        wv = tw(L::one(tp + v));
+      cum += (double)wv;
+      if (wv > 0.f) last_pos = v;
+      if (!s_fallback && cum > thr) {
+        tok = v;
+        break;
+      }
+    }
+    if (tok < 0) tok = last_pos;
+    a.out[R.trow] = tok;
+    if (a.resid_out) a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? s_Z : 0.0) : -1.f;
+  }
+}
+
+// ------------------------------------------------------------------ host helpers
+size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
+
+struct Sizes {
+  size_t off_hdr, off_req, off_rowdesc, off_resid, off_pt, off_pd, off_rp, total;
+};
+
+bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
+  if (B < 1 || K < 0 || V < 1 || V > (1ll << 30)) return false;
+  if (K + B >= (1ll << 29)) return false;
+  const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
+  if ((2 * K + B) * nseg >= (1ll << 31)) return false;
+  size_t o = 0;
+  z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
+  z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);
+  z->off_rowdesc = o; o = align_up(o + 4 * (size_t)(2 * K + B), 256);
+  z->off_resid = o; o = align_up(o + 4 * (size_t)B, 256);
+  z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)((K + B) * nseg), 256);
+  z->off_pd = o; o = align_up(o + sizeof(Partial) * (size_t)(K * nseg), 256);
+  z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nseg), 256);
+  z->total = o + 256;   // slack for aligning the caller's pointer
+  return true;
+}
+
+thread_local void* g_ev_begin = nullptr;
+thread_local void* g_ev_end = nullptr;
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count(int dev) {
+  if (dev >= 0 && dev < 64) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    c = 256;
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+void split_constant(double T, float* hi, float* lo, double* c64) {
+  const double c = 1.4426950408889634 / T;   // log2(e) / T
+  float h = (float)c;
+  if ((double)h > c) h = nextafterf(h, 0.f);  // round toward zero so that c_lo >= 0
+  float l = (float)(c - (double)h);
+  if (!(l >= 1e-30f)) l = 1e-30f;             // keep c_lo > 0: -inf * c_lo stays -inf
+  *hi = h;
+  *lo = l;
+  *c64 = c;
+}
+
+// Resident workgroups per CU for a kernel, from the occupancy calculator
+// (cached per device); the persistent grids are sized to exactly fill the chip.
+template <class Kern>
+int resident_blocks(std::atomic<int>* cache, Kern kern, int dev) {
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0) != hipSuccess || n <= 0)
+    n = 1;
+  n = std::min(n, kBlocksPerCU);
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <class L>
+void launch_all(const Args& a, hipStream_t st, int dev, bool sample) {
+  static std::atomic<int> occ_stats[64];
+  static std::atomic<int> occ_resid[64];
+  const long long cus = cu_count(dev);
+  const long long units_stats = (2ll * a.K + a.B) * a.nseg;
+  const long long units_resid = (long long)a.B * a.nseg;
+  const long long cap_s = cus * resident_blocks(occ_stats, k_stats<L>, dev);
+  const int grid_stats = (int)std::max(1ll, std::min(cap_s, (units_stats + kWavesPerBlock - 1) / kWavesPerBlock));
+  k_plan<<<1, kPlanThreads, 0, st>>>(a);
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
+  k_stats<L><<<grid_stats, kBlock, 0, st>>>(a);
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
+  k_decide<L><<<(a.B + kWavesPerBlock - 1) / kWavesPerBlock, kBlock, 0, st>>>(a);
+  if (sample) {
+    const long long cap_r = cus * resident_blocks(occ_resid, k_resid<L>, dev);
+    const int grid_resid = (int)std::max(1ll, std::min(cap_r, (units_resid + kWavesPerBlock - 1) / kWavesPerBlock));
+    k_resid<L><<<grid_resid, kBlock, 0, st>>>(a);
+    k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
+  }
+}
+
+int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t* gmask,
+            const float* u_accept, const float* u_final, int32_t* acc_len, int32_t* out,
+            float* p_out, float* q_out, float* resid_out, void* ws, size_t ws_bytes,
+            void* stream) {
+  // ---- host-side checks: nothing below touches the GPU until they pass
+  if (!bt) return SV_ERR_INVALID_ARG;
+  const long long B = bt->B, K = bt->K, V = bt->V;
+  Sizes z;
+  if (!compute_sizes(B, K, V, &z)) return SV_ERR_INVALID_ARG;
+  if (bt->dtype != SV_F32 && bt->dtype != SV_BF16) return SV_ERR_UNSUPPORTED;
+  const int es = bt->dtype == SV_F32 ? 4 : 2;
+  if (!bt->num_draft || !bt->target || !acc_len || !out) return SV_ERR_INVALID_ARG;
+  if (K > 0 && !bt->draft_tokens) return SV_ERR_INVALID_ARG;
+  if (bt->target_ld < V || bt->target_ld > (1ll << 40)) return SV_ERR_INVALID_ARG;
+  if ((uintptr_t)bt->target % es != 0) return SV_ERR_INVALID_ARG;
+  const bool need_draft = sample && K > 0;
+  if (sample) {
+    if (!u_final) return SV_ERR_INVALID_ARG;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
+    if (K > 0 && (!u_accept || !bt->draft)) return SV_ERR_INVALID_ARG;
+  }
+  if (need_draft) {
+    if (bt->draft_ld < V || bt->draft_ld > (1ll << 40)) return SV_ERR_INVALID_ARG;
+    if ((uintptr_t)bt->draft % es != 0) return SV_ERR_INVALID_ARG;
+  }
+  if (!ws) return SV_ERR_WORKSPACE;
+  if (ws_bytes < z.total) return SV_ERR_WORKSPACE;
+
+  // ---- argument block
+  const uintptr_t wb = align_up((uintptr_t)ws, 256);
+  Args a;
+  a.B = (int)B;
+  a.K = (int)K;
+  a.V = (int)V;
+  a.seg = kSegBytes / es;
+  a.nseg = (int)((V + a.seg - 1) / a.seg);
+  a.force_greedy = sample ? 0 : 1;
+  a.tld = bt->target_ld;
+  a.dld = need_draft ? bt->draft_ld : 0;
+  a.target = bt->target;
+  a.draft = need_draft ? bt->draft : nullptr;
+  a.num_draft = bt->num_draft;
+  a.tokens = bt->draft_tokens;
+  a.gmask = sample ? gmask : nullptr;
+  a.u_accept = u_accept;
+  a.u_final = u_final;
+  a.acc_len = acc_len;
+  a.out = out;
+  a.p_out = sample ? p_out : nullptr;
+  a.q_out = sample ? q_out : nullptr;
+  a.resid_out = sample ? resid_out : nullptr;
+  if (sample) {
+    a.T64 = (double)temperature;
+    split_constant(a.T64, &a.c_hi, &a.c_lo, &a.c64);
+  } else {
+    a.T64 = 1.0;
+    split_constant(1.0, &a.c_hi, &a.c_lo, &a.c64);
+  }
+  a.ws.hdr = reinterpret_cast<Header*>(wb + z.off_hdr);
+  a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);
+  a.ws.rowdesc = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc);
+  a.ws.resid_list = reinterpret_cast<int*>(wb + z.off_resid);
+  a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
+  a.ws.pd = reinterpret_cast<Partial*>(wb + z.off_pd);
+  a.ws.rp = reinterpret_cast<double*>(wb + z.off_rp);
+
+  bool vec = ((uintptr_t)bt->target % 16 == 0) && ((bt->target_ld * es) % 16 == 0);
+  if (need_draft) vec = vec && ((uintptr_t)bt->draft % 16 == 0) && ((bt->draft_ld * es) % 16 == 0);
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  (void)hipGetLastError();   // clear a stale error from earlier unrelated calls
+  if (bt->dtype == SV_F32) {
+    if (vec) launch_all<F32>(a, st, dev, sample);
+    else launch_all<Scalar<F32>>(a, st, dev, sample);
+  } else {
+    if (vec) launch_all<BF16>(a, st, dev, sample);
+    else launch_all<Scalar<BF16>>(a, st, dev, sample);
+  }
+  if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+}  // namespace
+
+extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+  Sizes z;
+  if (!compute_sizes(B, K, V, &z)) return 0;
+  return z.total;
+}
+
+extern "C" const char* spec_verify_status_string(int32_t status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED: return "unsupported dtype or dtype combination";
+    case SV_ERR_WORKSPACE: return "workspace missing or too small";
+    case SV_ERR_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t spec_verify_greedy(const sv_batch_t* batch, int32_t* accepted_len,
+                                      int32_t* out_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return run(batch, false, 1.f, nullptr, nullptr, nullptr, accepted_len, out_tokens, nullptr,
+             nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
+                                      const uint8_t* greedy_mask, const float* u_accept,
+                                      const float* u_final, int32_t* accepted_len,
+                                      int32_t* out_tokens, float* p_draft, float* q_draft,
+                                      float* resid_mass, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return run(batch, true, temperature, greedy_mask, u_accept, u_final, accepted_len, out_tokens,
+             p_draft, q_draft, resid_mass, workspace, workspace_bytes, stream);
+}
+
+extern "C" int32_t spec_verify_set_profile_events(void* ev_begin, void* ev_end) {
+  g_ev_begin = ev_begin;
+  g_ev_end = ev_end;
+  return SV_OK;
+}

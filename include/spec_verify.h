@@ -1,0 +1,139 @@
+/*
+ * spec_verify.h - C ABI of the one-round draft-token verification library
+ * (libspecverify.so, HIP for AMD Instinct MI355X / gfx950).
+ *
+ * The operation is the verification step of one speculative-decoding round as
+ * defined in chzhyang, "Speculative Decoding: Medusa, MTP, EAGLE, DFlash, DDTree,
+ * and DSpark", section 1, and the vLLM blog post "speculative-decoding-amd-gpus",
+ * section "Core idea of speculative decoding":
+ *
+ *   - drafts are checked left to right and the round is cut at the first
+ *     rejection; later drafts are discarded;
+ *   - stochastic requests keep draft y_i with probability min(1, p_i(y_i)/q_i(y_i)),
+ *     p_i = softmax(target logits / T), q_i = softmax(draft logits / T); at the
+ *     first rejection the correction is drawn from the normalised residual
+ *     [p_i - q_i]_+; if every draft survives a bonus token is drawn from the
+ *     target row that follows the last draft;
+ *   - greedy requests keep a draft while it equals the target argmax (lowest id
+ *     on ties) and commit the target's argmax at the first mismatch, or the
+ *     argmax of the bonus row when every draft survives.
+ *
+ * Randomness is supplied by the caller: one uniform u_i in [0,1) per draft
+ * position (keep iff u_i * q(y_i) < p(y_i)) and one uniform w_b in [0,1) per
+ * request for the single final draw, which takes the first token id t (in
+ * ascending id order) whose running sum of weights exceeds w_b times their
+ * total.  With the same inputs every call returns the same bits.
+ *
+ * Packed ragged layout.  Request b has k_b = num_draft[b] >= 0 drafts.  With
+ * off[b] = k_0 + ... + k_{b-1} and K = off[B]:
+ *   target row (b, i), i = 0..k_b  is row off[b] + b + i   (row k_b = bonus row)
+ *   draft  row (b, i), i < k_b     is row off[b] + i, draft token draft_tokens[off[b]+i]
+ *   out_tokens slot (b, i), i = 0..k_b is out_tokens[off[b] + b + i]
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers on the current HIP device, owned
+ *     by the caller.  The library allocates nothing and keeps no state between
+ *     calls; calls are asynchronous on `stream` (a hipStream_t, NULL = the
+ *     default stream) and results are valid once the stream reaches the call.
+ *   - Host-side argument checks run before any HIP call.  A failed check
+ *     returns an error status and launches nothing and writes nothing.
+ *   - SV_ERR_HIP reports a failed kernel launch (hipGetLastError).
+ *   - Device-side input problems are reported in the outputs, never by a
+ *     fault: if sum(num_draft) != K or some num_draft[b] < 0, every
+ *     accepted_len is -1 and every output slot is -1; a stochastic request
+ *     whose draft token lies outside [0, V) gets accepted_len -1 and all its
+ *     slots -1.  Greedy requests compare such a token like any other id.
+ *   - Logits must be finite or -inf, with at least one finite value per row;
+ *     NaN / +inf give unspecified (but in-range or -1) results.
+ *   - Unused out_tokens slots (after the committed a_b + 1 tokens) are -1.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad temperature, misalignment */
+  SV_ERR_UNSUPPORTED = 2,  /* dtype not supported, or target/draft dtypes differ   */
+  SV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required           */
+  SV_ERR_HIP = 4           /* a HIP call or kernel launch failed                   */
+} sv_status_t;
+
+typedef enum {
+  SV_F32 = 0,   /* IEEE binary32 logits                        */
+  SV_BF16 = 1   /* bfloat16 logits (upper half of a binary32)  */
+} sv_dtype_t;
+
+/* One packed batch of requests (see the layout above). */
+typedef struct sv_batch {
+  int32_t B;                  /* number of requests, >= 1                          */
+  int32_t K;                  /* total draft tokens, sum of num_draft, >= 0        */
+  int32_t V;                  /* vocabulary size, 1 <= V <= 2^30                   */
+  int32_t dtype;              /* sv_dtype_t of target and draft logits             */
+  int64_t target_ld;          /* elements between consecutive target rows, >= V    */
+  int64_t draft_ld;           /* elements between consecutive draft rows, >= V     */
+  const int32_t* num_draft;   /* device [B]: k_b                                   */
+  const void* target;         /* device [K+B][target_ld] logits                    */
+  const void* draft;          /* device [K][draft_ld] logits; may be NULL for
+                                 spec_verify_greedy                                */
+  const int32_t* draft_tokens;/* device [K]; may be NULL when K == 0               */
+} sv_batch_t;
+
+/* Bytes of device workspace a call with these sizes needs (256-byte aligned
+ * internally; any pointer alignment is accepted).  Returns 0 for invalid sizes. */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V);
+
+/* Static, NUL-terminated description of a status code. */
+const char* spec_verify_status_string(int32_t status);
+
+/* Greedy verification of every request (chzhyang section 1, "Greedy
+ * equivalence"; vLLM blog "A simple accept/reject example").  Reads target
+ * rows only.  Outputs:
+ *   accepted_len [B]  a_b = drafts kept (excludes the final target token)
+ *   out_tokens [K+B]  slots (b, 0..a_b-1) = kept drafts, slot (b, a_b) = target
+ *                     argmax of row (b, a_b), later slots -1.                  */
+int32_t spec_verify_greedy(const sv_batch_t* batch,
+                           int32_t* accepted_len, int32_t* out_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stochastic verification (chzhyang section 1: acceptance probability
+ * min(1, p/q), residual [p - q]_+ at the first rejection, bonus from the
+ * target), optionally mixed with greedy requests.
+ *   temperature   > 0 and finite; applied to target and draft logits alike.
+ *   greedy_mask   device [B] or NULL; a non-zero byte makes request b greedy
+ *                 (its draft rows, u_accept and u_final are then not read).
+ *   u_accept      device [K] uniforms in [0,1), one per draft position.
+ *   u_final       device [B] uniforms in [0,1), one per request.
+ *   accepted_len, out_tokens  as for spec_verify_greedy; slot (b, a_b) holds
+ *                 the correction or bonus draw.
+ *   p_draft, q_draft  device [K] or NULL: p(y_i), q(y_i) of every draft row of
+ *                 stochastic requests (also rows after the cut); -1 for greedy
+ *                 requests.
+ *   resid_mass    device [B] or NULL: total of [p - q]_+ at the cut (0 when it
+ *                 is zero and the draw fell back to p), -1 when the bonus was
+ *                 drawn or the request is greedy.                              */
+int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
+                           const uint8_t* greedy_mask,
+                           const float* u_accept, const float* u_final,
+                           int32_t* accepted_len, int32_t* out_tokens,
+                           float* p_draft, float* q_draft, float* resid_mass,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
+ * handles), later calls made from the calling thread record ev_begin just
+ * before and ev_end just after the row-statistics kernel, on the call's
+ * stream.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
+int32_t spec_verify_set_profile_events(void* ev_begin, void* ev_end);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,160 @@
+"""The C-ABI library loads, exports what its header declares, and rejects bad
+host arguments before touching the GPU (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+LIB = os.path.join(ROOT, "draft_token_verification_row_amd", "libspecverify.so")
+
+
+@pytest.fixture(scope="module")
+def sv():
+    if not os.path.exists(LIB):
+        from draft_token_verification_row_amd import build as b
+        b.build(verbose=False)
+    import draft_token_verification_row_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for need in ("spec_verify_greedy", "spec_verify_sample", "spec_verify_workspace_bytes",
+                 "spec_verify_status_string"):
+        assert need in names
+
+
+def test_library_exports_every_declared_symbol(sv):
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (spec_verify_\w+)", out))
+    assert set(declared_functions()) <= exported
+    assert set(sv.EXPORTED) == set(declared_functions())
+
+
+def test_status_strings(sv):
+    assert sv.spec_verify_status_string(0) == "ok"
+    for s in range(1, 5):
+        assert sv.spec_verify_status_string(s) not in ("ok", "unknown status")
+    assert sv.spec_verify_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(sv):
+    assert sv.spec_verify_workspace_bytes(0, 0, 10) == 0
+    assert sv.spec_verify_workspace_bytes(1, -1, 10) == 0
+    assert sv.spec_verify_workspace_bytes(1, 0, 0) == 0
+    assert sv.spec_verify_workspace_bytes(1, 0, (1 << 30) + 1) == 0
+    a = sv.spec_verify_workspace_bytes(64, 192, 32000)
+    b = sv.spec_verify_workspace_bytes(64, 192, 64000)
+    c = sv.spec_verify_workspace_bytes(128, 192, 32000)
+    assert 0 < a < b and a < c
+    # the largest workload needs a few MB, not a copy of the logits
+    assert sv.spec_verify_workspace_bytes(512, 3584, 262144) < 16 << 20
+
+
+FAKE = 1 << 20   # never dereferenced: every call below fails a host check first
+
+
+def _batch(sv, **kw):
+    d = dict(B=4, K=8, V=1000, dtype=0, target_ld=1000, draft_ld=1000, num_draft=FAKE,
+             target=FAKE, draft=FAKE, draft_tokens=FAKE)
+    d.update(kw)
+    return sv.SvBatch(**d)
+
+
+def _sample(sv, bt, T=1.0, ws_bytes=None, ws=FAKE, ua=FAKE, uf=FAKE, acc=FAKE, out=FAKE):
+    need = sv.spec_verify_workspace_bytes(max(bt.B, 1), max(bt.K, 0), max(bt.V, 1))
+    wsb = need if ws_bytes is None else ws_bytes
+    return sv._lib.spec_verify_sample(ctypes.byref(bt), ctypes.c_float(T), None, ua, uf, acc, out,
+                                      None, None, None, ws, wsb, None)
+
+
+def _greedy(sv, bt, ws_bytes=None, ws=FAKE, acc=FAKE, out=FAKE):
+    need = sv.spec_verify_workspace_bytes(max(bt.B, 1), max(bt.K, 0), max(bt.V, 1))
+    wsb = need if ws_bytes is None else ws_bytes
+    return sv._lib.spec_verify_greedy(ctypes.byref(bt), acc, out, ws, wsb, None)
+
+
+def test_host_validation_rejects_bad_arguments(sv):
+    INV, UNS, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED, sv.SV_ERR_WORKSPACE
+    assert sv._lib.spec_verify_sample(None, ctypes.c_float(1.0), None, FAKE, FAKE, FAKE, FAKE,
+                                      None, None, None, FAKE, 1 << 20, None) == INV
+    assert _sample(sv, _batch(sv, B=0)) == INV
+    assert _sample(sv, _batch(sv, K=-1)) == INV
+    assert _sample(sv, _batch(sv, V=0)) == INV
+    assert _sample(sv, _batch(sv, dtype=7)) == UNS
+    assert _sample(sv, _batch(sv, target_ld=999)) == INV
+    assert _sample(sv, _batch(sv, draft_ld=10)) == INV
+    assert _sample(sv, _batch(sv, num_draft=None)) == INV
+    assert _sample(sv, _batch(sv, target=None)) == INV
+    assert _sample(sv, _batch(sv, draft=None)) == INV
+    assert _sample(sv, _batch(sv, draft_tokens=None)) == INV
+    assert _sample(sv, _batch(sv, target=FAKE + 2)) == INV          # fp32 rows must be 4-byte aligned
+    assert _sample(sv, _batch(sv, dtype=1, target=FAKE + 1)) == INV  # bf16 rows 2-byte aligned
+    for T in (0.0, -1.0, float("nan"), float("inf")):
+        assert _sample(sv, _batch(sv), T=T) == INV, T
+    assert _sample(sv, _batch(sv), ua=None) == INV
+    assert _sample(sv, _batch(sv), uf=None) == INV
+    assert _sample(sv, _batch(sv), acc=None) == INV
+    assert _sample(sv, _batch(sv), out=None) == INV
+    assert _sample(sv, _batch(sv), ws=None) == WS
+    need = sv.spec_verify_workspace_bytes(4, 8, 1000)
+    assert _sample(sv, _batch(sv), ws_bytes=need - 1) == WS
+    # greedy: no draft, temperature or uniforms needed, but the same size checks
+    assert _greedy(sv, _batch(sv, B=0)) == INV
+    assert _greedy(sv, _batch(sv, target_ld=3)) == INV
+    assert _greedy(sv, _batch(sv), ws_bytes=need - 1) == WS
+    assert _greedy(sv, _batch(sv), out=None) == INV
+    # K = 0 needs no token pointer; still no launch because the workspace is short
+    assert _greedy(sv, _batch(sv, K=0, draft_tokens=None), ws_bytes=0) == WS
+
+
+def test_binding_argument_checks(sv):
+    import torch
+    t = torch.zeros(5, 10, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        sv.make_batch_struct(t, None, torch.zeros(1, dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32))
+    t = torch.zeros(10, 5).t()       # non-unit stride along the vocabulary
+    with pytest.raises(ValueError):
+        sv.make_batch_struct(t, None, torch.zeros(1, dtype=torch.int32),
+                             torch.zeros(4, dtype=torch.int32))
+
+
+def test_synthetic_layouts():
+    import synth
+    for cfg in (1, 2, 3, 4, 5):
+        b = synth.make_batch(cfg, B=6, V=257)
+        assert b.target.shape == (b.K + b.B, 257)
+        assert b.tokens.shape == (b.K,)
+        toks = b.tokens.numpy()
+        assert toks.min(initial=0) >= 0 and toks.max(initial=0) < 257
+        ua = b.u_accept.numpy().astype(np.float64)
+        assert np.all((ua >= 0) & (ua < 1)) and np.all(ua * 2 ** 24 == np.round(ua * 2 ** 24))
+        if cfg == 5:
+            assert set(np.unique(b.greedy)) <= {0, 1} and b.greedy[1] == 1 and b.greedy[0] == 0
+        if cfg == 2:
+            assert b.draft is None and b.temperature is None
+        else:
+            assert b.draft.shape == (b.K, 257)
+    # the same seed reproduces the batch
+    x, y = synth.make_batch(3, B=3, V=100), synth.make_batch(3, B=3, V=100)
+    assert torch_equal(x.target, y.target) and torch_equal(x.tokens, y.tokens)
+
+
+def torch_equal(a, b):
+    import torch
+    return bool(torch.equal(a, b))
