@@ -96,6 +96,18 @@ def cpu_baseline(batch, min_seconds: float, max_requests: int):
                        f"{t_total:.1f} s of fp64 NumPy on one host core")
 
 
+def copy_probe(mib: int, steps: int):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy-probe: {steps} copies of {mib} MiB ({mib * 1024} KiB read + written each)", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,7 +118,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps calls and exit without the JSON report (for rocprofv3)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe, args.steps)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

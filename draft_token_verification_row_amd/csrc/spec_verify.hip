@@ -41,6 +41,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "spec_verify.h"
 
@@ -49,9 +50,11 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = 8;           // 16-byte loads in flight per lane per row
+constexpr int kUnroll = 4;           // 16-byte loads in flight per lane per row
 constexpr int kSegBytes = 32768;     // one unit = 32 KiB of one logit row
 constexpr int kSegMinElems = kSegBytes / 4;
+constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
+constexpr int kRSegMinElems = kRSegBytes / 4;
 constexpr int kBlocksPerCU = 8;      // 32 wavefronts per CU
 constexpr int kPlanThreads = 1024;
 
@@ -91,11 +94,11 @@ struct Workspace {
   int* resid_list;     // [B]
   Partial* pt;         // [(K + B) * nseg]
   Partial* pd;         // [K * nseg]
-  double* rp;          // [B * nseg]
+  double* rp;          // [B * nrseg]
 };
 
 struct Args {
-  int B, K, V, nseg, seg;
+  int B, K, V, nseg, seg, nrseg, rseg;
   int force_greedy;
   int64_t tld, dld;
   const void* target;
@@ -116,12 +119,23 @@ struct Args {
 };
 
 // ------------------------------------------------------------------ element access
+// load():    ordinary 16-byte load (rescans of a single unit, gathers).
+// stream():  16-byte nontemporal load for data read once per call; it keeps the
+//            streamed logits from displacing other lines and measured faster on
+//            gfx950 for read-once sweeps.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 struct F32 {
   using Elem = float;
   static constexpr int E = 4;
   using Raw = float4;
   __device__ static __forceinline__ Raw load(const Elem* p) {
     return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ static __forceinline__ Raw stream(const Elem* p) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
   }
   __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
     v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
@@ -135,6 +149,10 @@ struct BF16 {
   using Raw = uint4;
   __device__ static __forceinline__ Raw load(const Elem* p) {
     return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ static __forceinline__ Raw stream(const Elem* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
   }
   __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
     v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
@@ -154,6 +172,7 @@ struct Scalar {
   static constexpr int E = 1;
   using Raw = float;
   __device__ static __forceinline__ Raw load(const Elem* p) { return D::one(p); }
+  __device__ static __forceinline__ Raw stream(const Elem* p) { return D::one(p); }
   __device__ static __forceinline__ void unpack(const Raw& r, float* v) { v[0] = r; }
   __device__ static __forceinline__ float one(const Elem* p) { return D::one(p); }
 };
@@ -192,7 +211,7 @@ __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, in
   for (int it = 0; it < nit; ++it, c += per_it) {
     typename L::Raw r[kUnroll];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) r[j] = L::load(p + (size_t)(c + j * kWave) * E);
+    for (int j = 0; j < kUnroll; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
 #pragma unroll
     for (int j = 0; j < kUnroll; ++j) {
       float v[E];
@@ -202,7 +221,7 @@ __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, in
   }
   for (; c < nchunk; c += kWave) {
     float v[E];
-    L::unpack(L::load(p + (size_t)c * E), v);
+    L::unpack(L::stream(p + (size_t)c * E), v);
     f(v, s0 + c * E, E);
   }
   const int tail0 = nchunk * E;
@@ -416,26 +435,67 @@ __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
 }
 
 // ------------------------------------------------------------------ row combines
-__device__ void combine_softmax(const Partial* P, int nseg, double T64, float& M, double& S) {
+// One lane combines the nseg unit partials of one row.  Loads are issued in
+// groups of 8 so that they are in flight together; unit factors use the same
+// split-constant exp2 as the streaming kernels and accumulate in fp64.
+constexpr int kCombineGroup = 8;
+
+__device__ void row_softmax(const Partial* P, int nseg, float c_hi, float c_lo, float& M,
+                            double& S) {
   float m = -FLT_MAX;
-  for (int s = 0; s < nseg; ++s) m = fmaxf(m, P[s].m);
-  double acc = 0.0;
-  for (int s = 0; s < nseg; ++s) {
-    const Partial p = P[s];
-    if (p.s > 0.0) acc += p.s * exp(((double)p.m - (double)m) / T64);
+  double s = 0.0;
+  for (int g0 = 0; g0 < nseg; g0 += kCombineGroup) {
+    float pm[kCombineGroup];
+    double ps[kCombineGroup];
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      if (g0 + j < nseg) {
+        const Partial p = P[g0 + j];
+        pm[j] = p.m;
+        ps[j] = p.s;
+      } else {
+        pm[j] = -FLT_MAX;
+        ps[j] = 0.0;
+      }
+    }
+    float gm = m;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) gm = fmaxf(gm, pm[j]);
+    if (gm > m) {
+      s *= (double)scaled_exp(m - gm, c_hi, c_lo);
+      m = gm;
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j)
+      if (ps[j] > 0.0) s += ps[j] * (double)scaled_exp(pm[j] - m, c_hi, c_lo);
   }
   M = m;
-  S = acc;
+  S = s;
 }
 
-__device__ void combine_argmax(const Partial* P, int nseg, int& idx) {
+__device__ void row_argmax(const Partial* P, int nseg, int& idx) {
   float bm = -INFINITY;
   int bi = INT_MAX;
-  for (int s = 0; s < nseg; ++s) {
-    const Partial p = P[s];
-    if (p.m > bm || (p.m == bm && p.idx < bi)) {
-      bm = p.m;
-      bi = p.idx;
+  for (int g0 = 0; g0 < nseg; g0 += kCombineGroup) {
+    float pm[kCombineGroup];
+    int pi[kCombineGroup];
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      if (g0 + j < nseg) {
+        const Partial p = P[g0 + j];
+        pm[j] = p.m;
+        pi[j] = p.idx;
+      } else {
+        pm[j] = -INFINITY;
+        pi[j] = INT_MAX;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      if (pm[j] > bm || (pm[j] == bm && pi[j] < bi)) {
+        bm = pm[j];
+        bi = pi[j];
+      }
     }
   }
   idx = bi;
@@ -447,6 +507,9 @@ __device__ __forceinline__ float logit_at(const void* base, int64_t row, int64_t
 }
 
 // ------------------------------------------------------------------ k_decide
+// One wavefront per request.  Positions are taken 32 at a time: lane l < 32
+// combines the target row of position base+l, lane l+32 the draft row of the
+// same position, so every row of a request is combined in parallel.
 template <class D>
 __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -473,29 +536,45 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
   const int drow0 = R.off;
   const bool g = R.greedy != 0;
   const int nseg = a.nseg;
-  int first_rej = k;
+  const int half = lane & 31;
+  const bool upper = lane >= 32;
+  int A = k;
+  bool found = false;       // A fixed (a rejection seen, or the bonus row reached)
   bool invalid = false;
-  for (int base = 0; base < k; base += kWave) {
-    const int i = base + lane;
+  float MpA = 0.f, MqA = 0.f;
+  double SpA = 0.0, SqA = 0.0;
+  int amaxA = INT_MAX;
+  for (int base = 0; base <= k; base += 32) {
+    const int i = base + half;
+    float M = 0.f;
+    double S = 0.0;
+    int amax = INT_MAX;
+    if (!upper && i <= k) {
+      const Partial* P = a.ws.pt + (int64_t)(trow0 + i) * nseg;
+      if (g)
+        row_argmax(P, nseg, amax);
+      else
+        row_softmax(P, nseg, a.c_hi, a.c_lo, M, S);
+    } else if (upper && !g && i < k) {
+      row_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.c_hi, a.c_lo, M, S);
+    }
+    const float Mq = __shfl(M, half + 32);
+    const double Sq = __shfl(S, half + 32);
     bool rej = false;
-    if (i < k) {
+    if (!upper && i < k) {
       const int y = a.tokens[drow0 + i];
       if (g) {
-        int idx;
-        combine_argmax(a.ws.pt + (int64_t)(trow0 + i) * nseg, nseg, idx);
-        rej = (y != idx);
+        rej = (y != amax);
+        if (a.p_out) a.p_out[drow0 + i] = -1.f;   // no probabilities for greedy rows
+        if (a.q_out) a.q_out[drow0 + i] = -1.f;
       } else if (y < 0 || y >= a.V) {
         invalid = true;
         if (a.p_out) a.p_out[drow0 + i] = -1.f;
         if (a.q_out) a.q_out[drow0 + i] = -1.f;
       } else {
-        float Mp, Mq;
-        double Sp, Sq;
-        combine_softmax(a.ws.pt + (int64_t)(trow0 + i) * nseg, nseg, a.T64, Mp, Sp);
-        combine_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.T64, Mq, Sq);
         const float zy = logit_at<D>(a.target, trow0 + i, a.tld, y);
         const float dy = logit_at<D>(a.draft, drow0 + i, a.dld, y);
-        const double py = exp(((double)zy - (double)Mp) / a.T64) / Sp;
+        const double py = exp(((double)zy - (double)M) / a.T64) / S;
         const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
         rej = !((double)a.u_accept[drow0 + i] * qy < py);
         if (a.p_out) a.p_out[drow0 + i] = (float)py;
@@ -503,8 +582,21 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
       }
     }
     const unsigned long long rm = __ballot(rej);
-    if (rm != 0ull && first_rej == k) first_rej = base + __ffsll((long long)rm) - 1;
-    if (g && first_rej < k) break;
+    if (!found && rm != 0ull) {
+      A = base + __ffsll((long long)rm) - 1;
+      found = true;
+    } else if (!found && k < base + 32) {
+      found = true;      // A = k, the bonus row lies in this chunk
+    }
+    if (found && A >= base && A < base + 32) {
+      const int src = A - base;
+      MpA = __shfl(M, src);
+      SpA = __shfl(S, src);
+      MqA = __shfl(M, src + 32);
+      SqA = __shfl(S, src + 32);
+      amaxA = __shfl(amax, src);
+    }
+    if (g && found) break;
   }
   if (__any(invalid)) {
     for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
@@ -515,18 +607,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
     }
     return;
   }
-  const int A = first_rej;
-  int final_tok = -1;
-  if (g) {
-    for (int i = lane; i < k; i += kWave) {   // no probabilities for greedy rows
-      if (a.p_out) a.p_out[drow0 + i] = -1.f;
-      if (a.q_out) a.q_out[drow0 + i] = -1.f;
-    }
-    int idx = INT_MAX;
-    if (lane == 0) combine_argmax(a.ws.pt + (int64_t)(trow0 + A) * nseg, nseg, idx);
-    idx = __shfl(idx, 0);
-    final_tok = (idx == INT_MAX) ? -1 : idx;
-  }
+  const int final_tok = g ? (amaxA == INT_MAX ? -1 : amaxA) : -1;
   for (int i = lane; i <= k; i += kWave) {
     int v = -1;
     if (i < A) v = a.tokens[drow0 + i];
@@ -542,12 +623,14 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
     if (g) {
       W.kind = KIND_NONE;
     } else {
-      combine_softmax(a.ws.pt + (int64_t)(trow0 + A) * nseg, nseg, a.T64, W.Mp, W.Sp);
+      W.Mp = MpA;
+      W.Sp = SpA;
       if (A < k) {
         W.kind = KIND_RESID;
         W.drow = drow0 + A;
         W.y = a.tokens[drow0 + A];
-        combine_softmax(a.ws.pd + (int64_t)(drow0 + A) * nseg, nseg, a.T64, W.Mq, W.Sq);
+        W.Mq = MqA;
+        W.Sq = SqA;
         const int j = atomicAdd(&a.ws.hdr->n_resid, 1);
         a.ws.resid_list[j] = b;
       } else {
@@ -560,7 +643,10 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
   }
 }
 
-// ------------------------------------------------------------------ residual weights
+// ------------------------------------------------------------------ draw weights
+// Residual weight [p - q]_+ and target weight p of one id, from the exact row
+// maxima and fp32 reciprocals of the row sums.  k_resid and k_finalize use
+// these same functions, so both see identical per-id values.
 struct ResidW {
   float Mp, Mq, ip, iq, c_hi, c_lo;
   __device__ __forceinline__ float operator()(float z, float d) const {
@@ -577,41 +663,53 @@ struct TargetW {
   }
 };
 
+__device__ __forceinline__ ResidW resid_weights(const ReqInfo& R, const Args& a) {
+  ResidW w;
+  w.Mp = R.Mp;
+  w.Mq = R.Mq;
+  w.ip = (float)(1.0 / R.Sp);
+  w.iq = (float)(1.0 / R.Sq);
+  w.c_hi = a.c_hi;
+  w.c_lo = a.c_lo;
+  return w;
+}
+
+__device__ __forceinline__ TargetW target_weights(const ReqInfo& R, const Args& a) {
+  TargetW w;
+  w.Mp = R.Mp;
+  w.ip = (float)(1.0 / R.Sp);
+  w.c_hi = a.c_hi;
+  w.c_lo = a.c_lo;
+  return w;
+}
+
 // ------------------------------------------------------------------ k_resid
+// Persistent grid; one wavefront per residual unit (rseg ids of one row pair).
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
   using Elem = typename L::Elem;
   constexpr int E = L::E;
+  constexpr int U = 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
-  const int n_units = a.ws.hdr->n_resid * a.nseg;
+  const int n_units = a.ws.hdr->n_resid * a.nrseg;
   for (int u = gw; u < n_units; u += W) {
-    const int j = u / a.nseg;
-    const int seg = u - j * a.nseg;
+    const int j = u / a.nrseg;
+    const int seg = u - j * a.nrseg;
     const int b = a.ws.resid_list[j];
     const ReqInfo R = a.ws.req[b];
-    ResidW fw;
-    fw.Mp = R.Mp;
-    fw.Mq = R.Mq;
-    fw.ip = (float)(1.0 / R.Sp);
-    fw.iq = (float)(1.0 / R.Sq);
-    fw.c_hi = a.c_hi;
-    fw.c_lo = a.c_lo;
+    const ResidW fw = resid_weights(R, a);
     const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
     const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
-    const int s0 = seg * a.seg;
-    const int s1 = min(s0 + a.seg, a.V);
+    const int s0 = seg * a.rseg;
+    const int s1 = min(s0 + a.rseg, a.V);
     const int n = s1 - s0;
     const int nchunk = n / E;
     const int y = R.y;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    constexpr int U = kUnroll / 2;
-    constexpr int per_it = kWave * U;
-    const int nit = nchunk / per_it;
-    int c = lane;
     auto chunk = [&](const typename L::Raw& rt, const typename L::Raw& rd, int id0) {
       float vt[E], vd[E];
       L::unpack(rt, vt);
@@ -627,18 +725,21 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += r[e];
     };
+    constexpr int per_it = kWave * U;
+    const int nit = nchunk / per_it;
+    int c = lane;
     for (int it = 0; it < nit; ++it, c += per_it) {
       typename L::Raw rt[U], rd[U];
 #pragma unroll
       for (int jj = 0; jj < U; ++jj) {
-        rt[jj] = L::load(tp + s0 + (size_t)(c + jj * kWave) * E);
-        rd[jj] = L::load(dp + s0 + (size_t)(c + jj * kWave) * E);
+        rt[jj] = L::stream(tp + s0 + (size_t)(c + jj * kWave) * E);
+        rd[jj] = L::stream(dp + s0 + (size_t)(c + jj * kWave) * E);
       }
 #pragma unroll
       for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
     }
     for (; c < nchunk; c += kWave)
-      chunk(L::load(tp + s0 + (size_t)c * E), L::load(dp + s0 + (size_t)c * E), s0 + c * E);
+      chunk(L::stream(tp + s0 + (size_t)c * E), L::stream(dp + s0 + (size_t)c * E), s0 + c * E);
     const int tail0 = nchunk * E;
     if (lane < n - tail0) {
       const int v = s0 + tail0 + lane;
@@ -648,194 +749,217 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) sl += acc[e];
     const double tot = wave_sum((double)sl);
-    if (lane == 0) a.ws.rp[(int64_t)b * a.nseg + seg] = tot;
+    if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
   }
 }
 
 // ------------------------------------------------------------------ k_finalize
-template <class L>
-__device__ __forceinline__ double range_sum_resid(const typename L::Elem* tp,
-                                                  const typename L::Elem* dp, int v0, int v1,
-                                                  const ResidW& fw, int y) {
-  constexpr int E = L::E;
-  double s = 0.0;
-  int v = v0;
-  for (; v + E <= v1; v += E) {
-    float vt[E], vd[E];
-    L::unpack(L::load(tp + v), vt);
-    L::unpack(L::load(dp + v), vd);
-    float cs = 0.f;
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) cs += (v + e == y) ? 0.f : fw(vt[e], vd[e]);
-    s += (double)cs;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  for (; v < v1; ++v) s += (v == y) ? 0.0 : (double)fw(L::one(tp + v), L::one(dp + v));
-  return s;
+  return x;
 }
 
-template <class L>
-__device__ __forceinline__ double range_sum_target(const typename L::Elem* tp, int v0, int v1,
-                                                   const TargetW& fw) {
-  constexpr int E = L::E;
-  double s = 0.0;
-  int v = v0;
-  for (; v + E <= v1; v += E) {
-    float vt[E];
-    L::unpack(L::load(tp + v), vt);
-    float cs = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) cs += fw(vt[e]);
-    s += (double)cs;
+// Mass of unit s for the draw: residual unit sums, or target mass of a
+// k_stats unit (its partial rescaled to the row maximum and sum).
+struct UnitMass {
+  const double* rp;
+  const Partial* prow;
+  float Mp, c_hi, c_lo;
+  double invSp;
+  bool resid;
+  __device__ __forceinline__ double operator()(int s) const {
+    if (resid) return rp[s];
+    const Partial p = prow[s];
+    return p.s > 0.0 ? p.s * (double)scaled_exp(p.m - Mp, c_hi, c_lo) * invSp : 0.0;
   }
-  for (; v < v1; ++v) s += (double)fw(L::one(tp + v));
-  return s;
+};
+
+// Wave 0 finds the unit holding the crossing of w * Z.  Returns (in lane 0's
+// view, broadcast) the unit, the cumulative mass before it and a fallback flag.
+__device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, double& Z,
+                          int& unit, double& before, int& fallback) {
+  double tot = 0.0;
+  for (int c0 = 0; c0 < nunits; c0 += kWave) {
+    const double m = (c0 + lane < nunits) ? um(c0 + lane) : 0.0;
+    tot += wave_sum(m);
+  }
+  Z = tot;
+  const double thr = w * Z;
+  double carry = 0.0;
+  unit = -1;
+  int last_pos = -1;
+  double last_before = 0.0;
+  for (int c0 = 0; c0 < nunits && unit < 0; c0 += kWave) {
+    const double m = (c0 + lane < nunits) ? um(c0 + lane) : 0.0;
+    const double incl = carry + wave_incl_scan(m, lane);
+    const double excl = incl - m;
+    const unsigned long long hit = __ballot(incl > thr && m > 0.0);
+    const unsigned long long pos = __ballot(m > 0.0);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      unit = c0 + src;
+      before = __shfl(excl, src);
+    } else if (pos) {
+      const int src = 63 - __clzll((long long)pos);
+      last_pos = c0 + src;
+      last_before = __shfl(excl, src);
+    }
+    carry = __shfl(incl, kWave - 1);
+  }
+  fallback = 0;
+  if (unit < 0) {      // rounding left w * Z at or past the end
+    unit = last_pos < 0 ? 0 : last_pos;
+    before = last_before;
+    fallback = 1;
+  }
+}
+
+// Rescan one unit of PER*kBlock ids with every weight cached in registers;
+// block-wide exclusive scan of the per-thread sums, then the owning thread walks
+// its ids in ascending order.
+template <class L, int PER, class WF>
+__device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* dp, int s0,
+                           int s1, int y, const WF& wf, double before, double thr, int fallback,
+                           double* s_wave, int* s_owner) {
+  constexpr int E = L::E;
+  static_assert(PER % E == 0, "per-thread ids must be whole chunks");
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
+  const int v0 = s0 + tid * PER;
+  float w[PER];
+#pragma unroll
+  for (int c = 0; c < PER / E; ++c) {
+    const int id0 = v0 + c * E;
+    float vt[E], vd[E];
+    if (id0 + E <= s1) {
+      L::unpack(L::load(tp + id0), vt);
+      if (dp) L::unpack(L::load(dp + id0), vd);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        vt[e] = (id0 + e < s1) ? L::one(tp + id0 + e) : -INFINITY;
+        vd[e] = (dp && id0 + e < s1) ? L::one(dp + id0 + e) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float x;
+      if constexpr (std::is_same<WF, ResidW>::value) x = wf(vt[e], vd[e]);
+      else x = wf(vt[e]);
+      w[c * E + e] = (id0 + e < s1 && id0 + e != y) ? x : 0.f;
+    }
+  }
+  double ts = 0.0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) ts += (double)w[j];
+  const double incl_w = wave_incl_scan(ts, lane);
+  if (lane == kWave - 1) s_wave[wv] = incl_w;
+  if (tid == 0) *s_owner = INT_MAX;
+  __syncthreads();
+  double wprefix = 0.0;
+  for (int q = 0; q < wv; ++q) wprefix += s_wave[q];
+  const double prev = __shfl_up(incl_w, 1);
+  const double excl = before + wprefix + (lane == 0 ? 0.0 : prev);
+  const double incl = before + wprefix + incl_w;
+  if (!fallback && incl > thr && ts > 0.0) atomicMin(s_owner, tid);
+  __syncthreads();
+  int owner = *s_owner;
+  if (owner == INT_MAX) {
+    // no thread crosses (rounding, or w*Z past the end): last thread with mass
+    __syncthreads();
+    if (tid == 0) *s_owner = -1;
+    __syncthreads();
+    if (ts > 0.0) atomicMax(s_owner, tid);
+    __syncthreads();
+    owner = *s_owner;
+    if (tid == owner) {
+      int tok = -1;
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (w[j] > 0.f) tok = v0 + j;
+      return tok;
+    }
+    return -2;
+  }
+  if (tid != owner) return -2;
+  double cum = excl;
+  int tok = -1, last = -1;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    cum += (double)w[j];
+    if (w[j] > 0.f) last = v0 + j;
+    if (tok < 0 && cum > thr) tok = v0 + j;
+  }
+  return tok >= 0 ? tok : last;
 }
 
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
   using Elem = typename L::Elem;
-  constexpr int E = L::E;
-  __shared__ double s_part[kBlock];
-  __shared__ double s_thr, s_base, s_Z;
-  __shared__ int s_seg, s_mode, s_j, s_fallback;
+  constexpr int PER_S = kSegBytes / (int)sizeof(Elem) / kBlock;    // k_stats unit
+  constexpr int PER_R = kRSegBytes / (int)sizeof(Elem) / kBlock;   // k_resid unit
+  __shared__ double s_wave[kWavesPerBlock];
+  __shared__ double s_before, s_thr, s_Z;
+  __shared__ int s_unit, s_mode, s_fallback, s_owner;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const int b = blockIdx.x;
   if (a.ws.hdr->error) return;
   const ReqInfo R = a.ws.req[b];
   if (R.kind != KIND_RESID && R.kind != KIND_BONUS) return;
-  const int nseg = a.nseg;
-  const Partial* prow = a.ws.pt + (int64_t)R.trow * nseg;
-  if (tid == 0) {
-    int mode = (R.kind == KIND_RESID) ? DRAW_RESID : DRAW_FROM_P;
-    double Z = 0.0;
-    if (mode == DRAW_RESID) {
-      for (int s = 0; s < nseg; ++s) Z += a.ws.rp[(int64_t)b * nseg + s];
-      if (!(Z > 0.0)) mode = DRAW_FROM_P;      // p == q numerically: draw from p
+  const double w = (double)a.u_final[b];
+  if (tid < kWave) {
+    UnitMass um;
+    um.rp = a.ws.rp + (int64_t)b * a.nrseg;
+    um.prow = a.ws.pt + (int64_t)R.trow * a.nseg;
+    um.Mp = R.Mp;
+    um.c_hi = a.c_hi;
+    um.c_lo = a.c_lo;
+    um.invSp = 1.0 / R.Sp;
+    um.resid = (R.kind == KIND_RESID);
+    int mode = um.resid ? DRAW_RESID : DRAW_FROM_P;
+    double Z = 0.0, before = 0.0;
+    int unit = 0, fb = 0;
+    find_unit(um, um.resid ? a.nrseg : a.nseg, w, lane, Z, unit, before, fb);
+    if (mode == DRAW_RESID && !(Z > 0.0)) {     // p == q numerically: draw from p
+      mode = DRAW_FROM_P;
+      um.resid = false;
+      find_unit(um, a.nseg, w, lane, Z, unit, before, fb);
     }
-    if (mode == DRAW_FROM_P) {
-      Z = 0.0;
-      for (int s = 0; s < nseg; ++s) {
-        const Partial p = prow[s];
-        if (p.s > 0.0) Z += p.s * exp(((double)p.m - (double)R.Mp) / a.T64) / R.Sp;
-      }
+    if (tid == 0) {
+      s_unit = unit;
+      s_before = before;
+      s_thr = w * Z;
+      s_Z = Z;
+      s_mode = mode;
+      s_fallback = fb;
     }
-    const double thr = (double)a.u_final[b] * Z;
-    double cum = 0.0;
-    int seg = -1, last_pos = -1;
-    double cum_last = 0.0;
-    for (int s = 0; s < nseg; ++s) {
-      double m;
-      if (mode == DRAW_RESID) {
-        m = a.ws.rp[(int64_t)b * nseg + s];
-      } else {
-        const Partial p = prow[s];
-        m = (p.s > 0.0) ? p.s * exp(((double)p.m - (double)R.Mp) / a.T64) / R.Sp : 0.0;
-      }
-      if (cum + m > thr) {
-        seg = s;
-        break;
-      }
-      if (m > 0.0) {
-        last_pos = s;
-        cum_last = cum;
-      }
-      cum += m;
-    }
-    s_fallback = 0;
-    if (seg < 0) {               // rounding left w*Z at or past the end
-      seg = last_pos < 0 ? 0 : last_pos;
-      cum = cum_last;
-      s_fallback = 1;
-    }
-    s_seg = seg;
-    s_base = cum;
-    s_thr = thr;
-    s_mode = mode;
-    s_Z = Z;
   }
   __syncthreads();
-  const int seg = s_seg;
   const int mode = s_mode;
-  const double thr = s_thr;
-  const int s0 = seg * a.seg;
-  const int s1 = min(s0 + a.seg, a.V);
-  const int n = s1 - s0;
-  int L_ = (n + kBlock - 1) / kBlock;
-  L_ = (L_ + E - 1) / E * E;
-  const int v0 = min(s0 + tid * L_, s1);
-  const int v1 = min(v0 + L_, s1);
   const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
-  const Elem* dp = (R.drow >= 0) ? static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld
-                                 : nullptr;
-  ResidW rw;
-  rw.Mp = R.Mp; rw.Mq = R.Mq;
-  rw.ip = (float)(1.0 / R.Sp);
-  rw.iq = (float)(1.0 / R.Sq);
-  rw.c_hi = a.c_hi; rw.c_lo = a.c_lo;
-  TargetW tw;
-  tw.Mp = R.Mp;
-  tw.ip = (float)(1.0 / R.Sp);
-  tw.c_hi = a.c_hi; tw.c_lo = a.c_lo;
-  const double mine = (mode == DRAW_RESID) ? range_sum_resid<L>(tp, dp, v0, v1, rw, R.y)
-                                           : range_sum_target<L>(tp, v0, v1, tw);
-  s_part[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {
-    double cum = s_base;
-    int j = -1, last = -1;
-    double cum_last = s_base;
-    if (!s_fallback) {
-      for (int t = 0; t < kBlock; ++t) {
-        if (cum + s_part[t] > thr) {
-          j = t;
-          break;
-        }
-        if (s_part[t] > 0.0) {
-          last = t;
-          cum_last = cum;
-        }
-        cum += s_part[t];
-      }
-    } else {
-      for (int t = 0; t < kBlock; ++t) {
-        if (s_part[t] > 0.0) {
-          last = t;
-          cum_last = cum;
-        }
-        cum += s_part[t];
-      }
-    }
-    int fb = s_fallback;
-    if (j < 0) {
-      j = last;
-      cum = cum_last;
-      fb = 1;
-    }
-    s_j = j;
-    s_base = cum;
-    s_fallback = fb;
+  int tok;
+  if (mode == DRAW_RESID) {
+    const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
+    const int s0 = s_unit * a.rseg;
+    const int s1 = min(s0 + a.rseg, a.V);
+    tok = rescan_unit<L, PER_R>(tp, dp, s0, s1, R.y, resid_weights(R, a), s_before, s_thr,
+                                s_fallback, s_wave, &s_owner);
+  } else {
+    const int s0 = s_unit * a.seg;
+    const int s1 = min(s0 + a.seg, a.V);
+    tok = rescan_unit<L, PER_S>(tp, (const Elem*)nullptr, s0, s1, -1, target_weights(R, a),
+                                s_before, s_thr, s_fallback, s_wave, &s_owner);
   }
-  __syncthreads();
-  if (tid == s_j) {
-    // walk this thread's ids in ascending order
-    double cum = s_base;
-    int tok = -1, last_pos = -1;
-    for (int v = v0; v < v1; ++v) {
-      float wv;
-      if (mode == DRAW_RESID)
-        wv = (v == R.y) ? 0.f : rw(L::one(tp + v), L::one(dp + v));
-      else
-        wv = tw(L::one(tp + v));
-      cum += (double)wv;
-      if (wv > 0.f) last_pos = v;
-      if (!s_fallback && cum > thr) {
-        tok = v;
-        break;
-      }
-    }
-    if (tok < 0) tok = last_pos;
+  if (tok != -2) {
     a.out[R.trow] = tok;
-    if (a.resid_out) a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? s_Z : 0.0) : -1.f;
+    if (a.resid_out)
+      a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? s_Z : 0.0) : -1.f;
   }
 }
 
@@ -850,7 +974,8 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   if (B < 1 || K < 0 || V < 1 || V > (1ll << 30)) return false;
   if (K + B >= (1ll << 29)) return false;
   const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
-  if ((2 * K + B) * nseg >= (1ll << 31)) return false;
+  const long long nrseg = (V + kRSegMinElems - 1) / kRSegMinElems;
+  if ((2 * K + B) * nseg >= (1ll << 31) || B * nrseg >= (1ll << 31)) return false;
   size_t o = 0;
   z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
   z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);
@@ -858,7 +983,7 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   z->off_resid = o; o = align_up(o + 4 * (size_t)B, 256);
   z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)((K + B) * nseg), 256);
   z->off_pd = o; o = align_up(o + sizeof(Partial) * (size_t)(K * nseg), 256);
-  z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nseg), 256);
+  z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nrseg), 256);
   z->total = o + 256;   // slack for aligning the caller's pointer
   return true;
 }
@@ -913,7 +1038,7 @@ void launch_all(const Args& a, hipStream_t st, int dev, bool sample) {
   static std::atomic<int> occ_resid[64];
   const long long cus = cu_count(dev);
   const long long units_stats = (2ll * a.K + a.B) * a.nseg;
-  const long long units_resid = (long long)a.B * a.nseg;
+  const long long units_resid = (long long)a.B * a.nrseg;
   const long long cap_s = cus * resident_blocks(occ_stats, k_stats<L>, dev);
   const int grid_stats = (int)std::max(1ll, std::min(cap_s, (units_stats + kWavesPerBlock - 1) / kWavesPerBlock));
   k_plan<<<1, kPlanThreads, 0, st>>>(a);
@@ -965,6 +1090,8 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.V = (int)V;
   a.seg = kSegBytes / es;
   a.nseg = (int)((V + a.seg - 1) / a.seg);
+  a.rseg = kRSegBytes / es;
+  a.nrseg = (int)((V + a.rseg - 1) / a.rseg);
   a.force_greedy = sample ? 0 : 1;
   a.tld = bt->target_ld;
   a.dld = need_draft ? bt->draft_ld : 0;
