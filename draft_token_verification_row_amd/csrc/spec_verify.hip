@@ -50,8 +50,14 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
-constexpr int kUnroll = 4;           // 16-byte loads in flight per lane per row
-constexpr int kSegBytes = 32768;     // one unit = 32 KiB of one logit row
+#ifndef SV_UNROLL
+#define SV_UNROLL 2
+#endif
+#ifndef SV_SEG_BYTES
+#define SV_SEG_BYTES 32768
+#endif
+constexpr int kUnroll = SV_UNROLL;       // 16-byte loads in flight per lane per row
+constexpr int kSegBytes = SV_SEG_BYTES;  // one unit = 32 KiB of one logit row
 constexpr int kSegMinElems = kSegBytes / 4;
 constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
 constexpr int kRSegMinElems = kRSegBytes / 4;
@@ -289,8 +295,8 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
 #pragma unroll
   for (int e = 0; e < L::E; ++e) sl += acc.s[e];
   const float mw = wave_max(acc.m);
-  const double f = exp2(((double)acc.m - (double)mw) * a.c64);
-  const double sw = wave_sum((double)sl * f);
+  const float f = scaled_exp(acc.m - mw, a.c_hi, a.c_lo);
+  const double sw = wave_sum((double)sl * (double)f);
   if (lane == 0) {
     Partial p;
     p.s = sw;
@@ -328,11 +334,25 @@ __device__ void argmax_unit(const typename L::Elem* row, int s0, int s1, int lan
 }
 
 // ------------------------------------------------------------------ k_plan
+__device__ __forceinline__ long long wave_incl_scan_ll(long long x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// One workgroup: exclusive scans of k_b (all requests) and of k_b over
+// stochastic requests, 1024 requests per pass (wave shuffles + one LDS step).
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
-  __shared__ long long sk[kPlanThreads];
-  __shared__ long long ss[kPlanThreads];
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  __shared__ long long s_wk[kPlanWaves];
+  __shared__ long long s_ws[kPlanWaves];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
   if (tid == 0) s_bad = 0;
   __syncthreads();
   const long long TB = (long long)a.K + a.B;
@@ -351,21 +371,24 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
     }
     const long long ks = g ? 0 : k;
-    sk[tid] = k;
-    ss[tid] = ks;
-    __syncthreads();
-    for (int o = 1; o < kPlanThreads; o <<= 1) {
-      const long long xk = tid >= o ? sk[tid - o] : 0;
-      const long long xs = tid >= o ? ss[tid - o] : 0;
-      __syncthreads();
-      sk[tid] += xk;
-      ss[tid] += xs;
-      __syncthreads();
+    const long long ik = wave_incl_scan_ll(k, lane);
+    const long long is = wave_incl_scan_ll(ks, lane);
+    if (lane == kWave - 1) {
+      s_wk[wv] = ik;
+      s_ws[wv] = is;
     }
-    const long long off = carry_k + sk[tid] - k;
-    const long long soff = carry_s + ss[tid] - ks;
-    const long long tot_k = sk[kPlanThreads - 1];
-    const long long tot_s = ss[kPlanThreads - 1];
+    __syncthreads();
+    long long pk = 0, ps = 0, tot_k = 0, tot_s = 0;
+    for (int q = 0; q < kPlanWaves; ++q) {
+      if (q < wv) {
+        pk += s_wk[q];
+        ps += s_ws[q];
+      }
+      tot_k += s_wk[q];
+      tot_s += s_ws[q];
+    }
+    const long long off = carry_k + pk + ik - k;
+    const long long soff = carry_s + ps + is - ks;
     if (b < a.B) {
       ReqInfo r;
       r.off = (int)off;
@@ -407,6 +430,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
 }
 
 // ------------------------------------------------------------------ k_stats
+// Persistent grid; wavefront gw takes units gw, gw + W, ...  The descriptor of
+// the next unit is fetched while the current one streams.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
   using Elem = typename L::Elem;
@@ -416,10 +441,12 @@ __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
   const int n_units = a.ws.hdr->n_units;
   const Elem* tgt = static_cast<const Elem*>(a.target);
   const Elem* drf = static_cast<const Elem*>(a.draft);
+  uint32_t next = (gw < n_units) ? a.ws.rowdesc[gw / a.nseg] : 0u;
   for (int u = gw; u < n_units; u += W) {
+    const uint32_t desc = next;
     const int ri = u / a.nseg;
     const int seg = u - ri * a.nseg;
-    const uint32_t desc = a.ws.rowdesc[ri];
+    if (u + W < n_units) next = a.ws.rowdesc[(u + W) / a.nseg];
     const int row = (int)(desc & kRowMask);
     const bool is_draft = (desc & kDraftBit) != 0;
     const bool greedy = (desc & kGreedyBit) != 0;
@@ -546,6 +573,18 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
   int amaxA = INT_MAX;
   for (int base = 0; base <= k; base += 32) {
     const int i = base + half;
+    // issue the gathers at y first; they do not depend on the row statistics
+    int y = 0;
+    bool yok = false;
+    float zy = 0.f, dy = 0.f;
+    if (!upper && i < k) {
+      y = a.tokens[drow0 + i];
+      yok = (y >= 0 && y < a.V);
+      if (!g && yok) {
+        zy = logit_at<D>(a.target, trow0 + i, a.tld, y);
+        dy = logit_at<D>(a.draft, drow0 + i, a.dld, y);
+      }
+    }
     float M = 0.f;
     double S = 0.0;
     int amax = INT_MAX;
@@ -562,18 +601,15 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
     const double Sq = __shfl(S, half + 32);
     bool rej = false;
     if (!upper && i < k) {
-      const int y = a.tokens[drow0 + i];
       if (g) {
         rej = (y != amax);
         if (a.p_out) a.p_out[drow0 + i] = -1.f;   // no probabilities for greedy rows
         if (a.q_out) a.q_out[drow0 + i] = -1.f;
-      } else if (y < 0 || y >= a.V) {
+      } else if (!yok) {
         invalid = true;
         if (a.p_out) a.p_out[drow0 + i] = -1.f;
         if (a.q_out) a.q_out[drow0 + i] = -1.f;
       } else {
-        const float zy = logit_at<D>(a.target, trow0 + i, a.tld, y);
-        const float dy = logit_at<D>(a.draft, drow0 + i, a.dld, y);
         const double py = exp(((double)zy - (double)M) / a.T64) / S;
         const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
         rej = !((double)a.u_accept[drow0 + i] * qy < py);
@@ -693,15 +729,27 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
-  const int n_units = a.ws.hdr->n_resid * a.nrseg;
-  for (int u = gw; u < n_units; u += W) {
+  // each wavefront takes a contiguous range of units, so consecutive units
+  // mostly share a request and its record is fetched once
+  const long long n_units = (long long)a.ws.hdr->n_resid * a.nrseg;
+  const int u_begin = (int)(n_units * gw / W);
+  const int u_end = (int)(n_units * (gw + 1) / W);
+  int cur = -1, b = 0;
+  ReqInfo R;
+  ResidW fw;
+  const Elem* tp = nullptr;
+  const Elem* dp = nullptr;
+  for (int u = u_begin; u < u_end; ++u) {
     const int j = u / a.nrseg;
     const int seg = u - j * a.nrseg;
-    const int b = a.ws.resid_list[j];
-    const ReqInfo R = a.ws.req[b];
-    const ResidW fw = resid_weights(R, a);
-    const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
-    const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
+    if (j != cur) {
+      cur = j;
+      b = a.ws.resid_list[j];
+      R = a.ws.req[b];
+      fw = resid_weights(R, a);
+      tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
+      dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
+    }
     const int s0 = seg * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
     const int n = s1 - s0;
@@ -782,10 +830,13 @@ struct UnitMass {
 // view, broadcast) the unit, the cumulative mass before it and a fallback flag.
 __device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, double& Z,
                           int& unit, double& before, int& fallback) {
+  // Z is the total of the same chunked scan that locates the crossing, so the
+  // two agree bit for bit; with <= 64 units (the usual case) masses load once.
+  double m0 = (lane < nunits) ? um(lane) : 0.0;
   double tot = 0.0;
   for (int c0 = 0; c0 < nunits; c0 += kWave) {
-    const double m = (c0 + lane < nunits) ? um(c0 + lane) : 0.0;
-    tot += wave_sum(m);
+    const double m = (c0 == 0) ? m0 : ((c0 + lane < nunits) ? um(c0 + lane) : 0.0);
+    tot = __shfl(tot + wave_incl_scan(m, lane), kWave - 1);
   }
   Z = tot;
   const double thr = w * Z;
@@ -794,7 +845,7 @@ __device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, do
   int last_pos = -1;
   double last_before = 0.0;
   for (int c0 = 0; c0 < nunits && unit < 0; c0 += kWave) {
-    const double m = (c0 + lane < nunits) ? um(c0 + lane) : 0.0;
+    const double m = (c0 == 0) ? m0 : ((c0 + lane < nunits) ? um(c0 + lane) : 0.0);
     const double incl = carry + wave_incl_scan(m, lane);
     const double excl = incl - m;
     const unsigned long long hit = __ballot(incl > thr && m > 0.0);
