@@ -28,7 +28,7 @@ Pages cited:
 * The accepted length excludes the correction/bonus token ([CZ] section 2,
   definition of A).
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
   R1  p = softmax(z / T), q = softmax(d / T), the same fp32 temperature T for
       both, widened exactly to fp64.
   R2  Greedy ignores T and takes the lowest token id among tied maxima.
