@@ -314,3 +314,36 @@ def pin_packed_batch(vm):
 ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ties,
             pin_exact_distribution_quadrature, pin_special_cases, pin_greedy_invariants,
             pin_packed_batch]
+
+
+# ---------------------------------------------------------------- acceptance statistics
+def pin_acceptance_appendix(am, B: int = 20000):
+    """Rounds built so that #{A >= j} / B equals each printed p_j reproduce the
+    printed MAL (within the tables' 2-decimal rounding of MAL and percent
+    rounding of p_j) and AR ([VLLM] Appendix; MAL counts the final token)."""
+    g = load_golden("appendix_acceptance.json")
+    for r in g["rows"]:
+        N = r["N"]
+        c = [int(round(p / 100.0 * B)) for p in r["p"]] + [0]
+        acc = []
+        acc += [0] * (B - c[0])
+        for j in range(1, N + 1):
+            acc += [j] * (c[j - 1] - c[j])
+        st = am.acceptance_stats(np.array(acc), np.full(B, N), N)
+        assert st["rounds"] == B
+        assert np.allclose(st["per_position"], np.array(r["p"]) / 100.0, atol=1.0 / B), (r, st)
+        assert abs(st["mal"] - r["MAL"]) <= 0.03, (r["table"], N, st["mal"], r["MAL"])
+        assert abs(100.0 * st["ar"] - r["AR"]) <= 0.6, (r["table"], N, st["ar"], r["AR"])
+        assert abs(st["ar"] - (st["mal"] - 1.0) / N) < 1e-12
+
+
+def pin_acceptance_ragged(am):
+    """Hand-derived ragged case: per-position denominators count only rounds that
+    proposed position j; invalid rounds (accepted length -1) are ignored."""
+    st = am.acceptance_stats(np.array([2, 1, 0, 0, -1]), np.array([3, 1, 0, 2, 5]), 4)
+    assert st["rounds"] == 4
+    assert st["mean_accepted"] == 0.75 and st["mal"] == 1.75 and st["ar"] == 0.5
+    assert np.allclose(st["per_position"], [2 / 3, 1 / 2, 0.0, -1.0], rtol=0, atol=1e-15)
+
+
+ACCEPT_PINS = [pin_acceptance_appendix, pin_acceptance_ragged]
