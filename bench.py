@@ -246,6 +246,13 @@ def main():
             "avg_kernel_ms": t_stats * 1e3,
         },
     }
+    kmax = int(batch.num_draft.max()) if batch.K > 0 else 1
+    st = sv.spec_verify_accept_stats(acc, nd, max(kmax, 1)).cpu().numpy()
+    res["acceptance"] = {
+        "note": "from the timed calls' outputs; MAL counts the correction/bonus token, AR = kept/proposed drafts",
+        "mean_kept_drafts": float(st[1]), "MAL": float(st[2]), "AR": float(st[3]),
+        "per_position": [round(float(x), 4) for x in st[4:4 + max(kmax, 1)]],
+    }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, max_requests=batch.B)
     print(json.dumps(res), flush=True)

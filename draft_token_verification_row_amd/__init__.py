@@ -24,7 +24,8 @@ _DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
 
 # Every function the C header declares (checked by the CPU test suite).
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
-            "spec_verify_greedy", "spec_verify_sample", "spec_verify_set_profile_events")
+            "spec_verify_greedy", "spec_verify_sample", "spec_verify_accept_stats",
+            "spec_verify_set_profile_events")
 
 
 class SvBatch(ctypes.Structure):
@@ -53,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_sample.argtypes = [ctypes.POINTER(SvBatch), ctypes.c_float, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.restype = i32
+    lib.spec_verify_accept_stats.argtypes = [vp, vp, i32, i32, vp, vp]
+    lib.spec_verify_accept_stats.restype = i32
     lib.spec_verify_set_profile_events.argtypes = [vp, vp]
     lib.spec_verify_set_profile_events.restype = i32
     return lib
@@ -170,6 +173,23 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
         raise SpecVerifyError(st)
     return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,
                 q_draft=q_draft, resid_mass=resid_mass)
+
+
+def spec_verify_accept_stats(accepted_len: torch.Tensor, num_draft: torch.Tensor, max_pos: int,
+                             *, out=None, stream=None) -> torch.Tensor:
+    """Acceptance statistics of one call's outcome; returns a float64 device tensor
+    [4 + max_pos]: rounds, mean kept drafts, MAL (counts the final token), AR,
+    per-position acceptance p_1..p_max_pos (-1 where undefined)."""
+    B = int(accepted_len.numel())
+    if int(num_draft.numel()) != B:
+        raise ValueError("accepted_len and num_draft must have the same length")
+    if out is None:
+        out = torch.empty(4 + max_pos, dtype=torch.float64, device=accepted_len.device)
+    st = _lib.spec_verify_accept_stats(_ptr(accepted_len), _ptr(num_draft), B, max_pos, _ptr(out),
+                                       _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return out
 
 
 def verify_batch(batch, *, workspace=None, want_probs=True, stream=None):

@@ -126,6 +126,23 @@ int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
                            float* p_draft, float* q_draft, float* resid_mass,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Acceptance statistics of verification outcomes, the signals of the vLLM blog
+ * post "speculative-decoding-amd-gpus" ("Monitor acceptance behavior", and the
+ * per-position columns of its Appendix tables).  Inputs are the accepted_len
+ * [B] a call produced and the num_draft [B] it was given (device arrays);
+ * rounds with accepted_len < 0 are not counted.  Writes device out[4 + max_pos]
+ * (doubles):
+ *   out[0] rounds counted n
+ *   out[1] mean kept drafts  sum(a) / n                       (-1 if n == 0)
+ *   out[2] MAL = 1 + out[1]: counts the correction/bonus token (-1 if n == 0)
+ *   out[3] AR  = sum(a) / sum(k), kept over proposed drafts    (-1 if sum(k) == 0)
+ *   out[3 + j], j = 1..max_pos: #{a >= j} / #{k >= j}         (-1 if no round
+ *          proposed position j)
+ * 1 <= max_pos <= 4096; host checks as for the other entry points.  One
+ * workgroup; intended for batches of up to a few hundred thousand rounds. */
+int32_t spec_verify_accept_stats(const int32_t* accepted_len, const int32_t* num_draft,
+                                 int32_t B, int32_t max_pos, double* out, void* stream);
+
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
  * before and ev_end just after the row-statistics kernel, on the call's

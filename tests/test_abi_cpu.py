@@ -158,3 +158,14 @@ def test_synthetic_layouts():
 def torch_equal(a, b):
     import torch
     return bool(torch.equal(a, b))
+
+
+def test_accept_stats_host_validation(sv):
+    INV = sv.SV_ERR_INVALID_ARG
+    f = sv._lib.spec_verify_accept_stats
+    assert f(None, FAKE, 4, 3, FAKE, None) == INV
+    assert f(FAKE, None, 4, 3, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 3, None, None) == INV
+    assert f(FAKE, FAKE, 0, 3, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 0, FAKE, None) == INV
+    assert f(FAKE, FAKE, 4, 4097, FAKE, None) == INV
