@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps calls and exit without the JSON report (for rocprofv3)")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="time the early-exit entry points (rows read only up to each cut)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -157,18 +159,30 @@ def main():
     sh = stream.cuda_stream
     lib = sv._lib
     greedy_only = batch.temperature is None
+    kmax = int(batch.num_draft.max()) if batch.K > 0 else 0
+    ee = args.early_exit
     if greedy_only:
-        def call():
-            return lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
-                                          ws.data_ptr(), ws_bytes, sh)
+        if ee:
+            def call():
+                return lib.spec_verify_greedy_early_exit(ctypes.byref(bt), kmax, acc.data_ptr(),
+                                                         out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+        else:
+            def call():
+                return lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
+                                              ws.data_ptr(), ws_bytes, sh)
     else:
         T = ctypes.c_float(batch.temperature)
         a_ptrs = (gm.data_ptr() if gm is not None else None, batch.u_accept.data_ptr(),
                   batch.u_final.data_ptr(), acc.data_ptr(), out.data_ptr(), pdr.data_ptr(),
                   qdr.data_ptr(), rm.data_ptr())
-
-        def call():
-            return lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes, sh)
+        if ee:
+            def call():
+                return lib.spec_verify_sample_early_exit(ctypes.byref(bt), kmax, T, *a_ptrs,
+                                                         ws.data_ptr(), ws_bytes, sh)
+        else:
+            def call():
+                return lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes,
+                                              sh)
 
     for _ in range(args.warmup):
         assert call() == 0
@@ -199,6 +213,12 @@ def main():
     es = 4 if batch.dtype == "f32" else 2
     stoch_draft_rows = 0 if greedy_only else int(batch.num_draft[batch.greedy == 0].sum())
     rows = batch.K + batch.B + stoch_draft_rows
+    if ee:
+        # rows up to each request's cut: a_b + 1 target rows, min(a_b + 1, k_b) draft rows
+        a_np = acc.cpu().numpy().astype(np.int64)
+        k_np = batch.num_draft.astype(np.int64)
+        stoch = np.zeros(batch.B, bool) if greedy_only else (batch.greedy == 0)
+        rows = int((a_np + 1).sum() + np.minimum(a_np + 1, k_np)[stoch].sum())
     bytes_stats = rows * batch.V * es                 # every row the kernel must read, once
     t_stats = float(np.mean(stats_ms)) / 1e3
     achieved = bytes_stats / t_stats / 1e9
@@ -230,12 +250,14 @@ def main():
             "requests": ("greedy" if greedy_only else
                          f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
             "parallelism": "single GPU",
+            "path": "early exit (max_k = %d)" % kmax if ee else "all rows",
         },
         "rows_per_s": (batch.K + batch.B) / step_s,
         "hbm_gbs_step": bytes_stats / step_s / 1e9,
         "hbm_frac_step": bytes_stats / step_s / 1e9 / PEAK_HBM_GBS,
         "roofline": {
-            "kernel": "k_stats (row statistics)",
+            "kernel": ("rounds: k_stats + k_decide_round per position" if ee
+                       else "k_stats (row statistics)"),
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,
@@ -246,7 +268,6 @@ def main():
             "avg_kernel_ms": t_stats * 1e3,
         },
     }
-    kmax = int(batch.num_draft.max()) if batch.K > 0 else 1
     st = sv.spec_verify_accept_stats(acc, nd, max(kmax, 1)).cpu().numpy()
     res["acceptance"] = {
         "note": "from the timed calls' outputs; MAL counts the correction/bonus token, AR = kept/proposed drafts",

@@ -24,7 +24,8 @@ _DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
 
 # Every function the C header declares (checked by the CPU test suite).
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
-            "spec_verify_greedy", "spec_verify_sample", "spec_verify_accept_stats",
+            "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_early_exit",
+            "spec_verify_sample_early_exit", "spec_verify_accept_stats",
             "spec_verify_set_profile_events")
 
 
@@ -54,6 +55,12 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_sample.argtypes = [ctypes.POINTER(SvBatch), ctypes.c_float, vp, vp, vp,
                                        vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample.restype = i32
+    lib.spec_verify_greedy_early_exit.argtypes = [ctypes.POINTER(SvBatch), i32, vp, vp, vp, sz,
+                                                  vp]
+    lib.spec_verify_greedy_early_exit.restype = i32
+    lib.spec_verify_sample_early_exit.argtypes = [ctypes.POINTER(SvBatch), i32, ctypes.c_float,
+                                                  vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_sample_early_exit.restype = i32
     lib.spec_verify_accept_stats.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.spec_verify_accept_stats.restype = i32
     lib.spec_verify_set_profile_events.argtypes = [vp, vp]
@@ -125,8 +132,12 @@ def _workspace(B, K, V, workspace, device):
 
 
 def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, num_draft: torch.Tensor,
-                       *, accepted_len=None, out_tokens=None, workspace=None, stream=None):
-    """Greedy verification; returns (accepted_len [B], out_tokens [K+B]) int32 tensors."""
+                       *, accepted_len=None, out_tokens=None, workspace=None, stream=None,
+                       max_k: Optional[int] = None):
+    """Greedy verification; returns (accepted_len [B], out_tokens [K+B]) int32 tensors.
+
+    With max_k given, calls spec_verify_greedy_early_exit (reads rows only up to
+    each request's cut; every num_draft[b] must be <= max_k)."""
     bt = make_batch_struct(target, None, draft_tokens, num_draft)
     dev = target.device
     if accepted_len is None:
@@ -134,8 +145,13 @@ def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, num_dra
     if out_tokens is None:
         out_tokens = torch.empty(bt.K + bt.B, dtype=torch.int32, device=dev)
     workspace, wsb = _workspace(bt.B, bt.K, bt.V, workspace, dev)
-    st = _lib.spec_verify_greedy(ctypes.byref(bt), _ptr(accepted_len), _ptr(out_tokens),
-                                 _ptr(workspace), wsb, _stream_handle(stream))
+    if max_k is None:
+        st = _lib.spec_verify_greedy(ctypes.byref(bt), _ptr(accepted_len), _ptr(out_tokens),
+                                     _ptr(workspace), wsb, _stream_handle(stream))
+    else:
+        st = _lib.spec_verify_greedy_early_exit(ctypes.byref(bt), int(max_k), _ptr(accepted_len),
+                                                _ptr(out_tokens), _ptr(workspace), wsb,
+                                                _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accepted_len, out_tokens
@@ -145,11 +161,13 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
                        draft_tokens: torch.Tensor, num_draft: torch.Tensor, temperature: float,
                        u_accept: torch.Tensor, u_final: torch.Tensor, *, greedy_mask=None,
                        accepted_len=None, out_tokens=None, p_draft=None, q_draft=None,
-                       resid_mass=None, want_probs: bool = True, workspace=None, stream=None):
+                       resid_mass=None, want_probs: bool = True, workspace=None, stream=None,
+                       max_k: Optional[int] = None):
     """Stochastic (optionally mixed greedy) verification.
 
     Returns a dict of device tensors: accepted_len, out_tokens, p_draft, q_draft,
     resid_mass (the last three None when want_probs is False and none was given).
+    With max_k given, calls spec_verify_sample_early_exit.
     """
     bt = make_batch_struct(target, draft, draft_tokens, num_draft)
     dev = target.device
@@ -165,10 +183,13 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
         if resid_mass is None:
             resid_mass = torch.empty(bt.B, dtype=torch.float32, device=dev)
     workspace, wsb = _workspace(bt.B, bt.K, bt.V, workspace, dev)
-    st = _lib.spec_verify_sample(
-        ctypes.byref(bt), ctypes.c_float(temperature), _ptr(greedy_mask), _ptr(u_accept),
-        _ptr(u_final), _ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
-        _ptr(resid_mass), _ptr(workspace), wsb, _stream_handle(stream))
+    rest = (ctypes.c_float(temperature), _ptr(greedy_mask), _ptr(u_accept), _ptr(u_final),
+            _ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(resid_mass),
+            _ptr(workspace), wsb, _stream_handle(stream))
+    if max_k is None:
+        st = _lib.spec_verify_sample(ctypes.byref(bt), *rest)
+    else:
+        st = _lib.spec_verify_sample_early_exit(ctypes.byref(bt), int(max_k), *rest)
     if st != SV_OK:
         raise SpecVerifyError(st)
     return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,
@@ -192,12 +213,13 @@ def spec_verify_accept_stats(accepted_len: torch.Tensor, num_draft: torch.Tensor
     return out
 
 
-def verify_batch(batch, *, workspace=None, want_probs=True, stream=None):
-    """Run a synthetic batch object (fields as produced by the input generator)."""
+def verify_batch(batch, *, workspace=None, want_probs=True, stream=None, max_k=None):
+    """Run a synthetic batch object (fields as produced by the input generator).
+    max_k selects the early-exit entry points."""
     nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=batch.target.device)
     if batch.temperature is None:
         acc, out = spec_verify_greedy(batch.target, batch.tokens, nd, workspace=workspace,
-                                      stream=stream)
+                                      stream=stream, max_k=max_k)
         return dict(accepted_len=acc, out_tokens=out, p_draft=None, q_draft=None,
                     resid_mass=None)
     gm = None
@@ -205,4 +227,5 @@ def verify_batch(batch, *, workspace=None, want_probs=True, stream=None):
         gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=batch.target.device)
     return spec_verify_sample(batch.target, batch.draft, batch.tokens, nd, batch.temperature,
                               batch.u_accept, batch.u_final, greedy_mask=gm,
-                              want_probs=want_probs, workspace=workspace, stream=stream)
+                              want_probs=want_probs, workspace=workspace, stream=stream,
+                              max_k=max_k)

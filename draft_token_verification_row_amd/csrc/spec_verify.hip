@@ -5,7 +5,8 @@
 // Decoding: Medusa, MTP, EAGLE, DFlash, DDTree, and DSpark", section 1; vLLM blog
 // "speculative-decoding-amd-gpus", "Core idea of speculative decoding").
 //
-// Pipeline (all launches on the caller's stream, no host synchronisation):
+// All-rows pipeline (spec_verify_greedy / spec_verify_sample; every launch on
+// the caller's stream, no host synchronisation):
 //   k_plan      one workgroup: exclusive scan of num_draft -> request offsets,
 //               compact list of logit rows to read (every target row, the draft
 //               rows of stochastic requests), unit count.
@@ -25,6 +26,11 @@
 //               the inverse-CDF crossing from the unit sums (bonus: from the
 //               k_stats partials, no re-read), rescans that unit only and writes
 //               the correction / bonus token.
+//
+// Early-exit pipeline (the *_early_exit entry points): k_plan_ee, then per
+// draft position j a k_round launch (row statistics of position j of the
+// requests still undecided, residual sweeps of the requests cut at j - 1) and a
+// k_decide_round launch (decides position j), then k_finalize.
 //
 // Numerics.  exp((z - m)/T) is evaluated as exp2((z - m) * c) with
 // c = log2(e)/T split into two fp32 constants (c_hi + c_lo), so the rounding of
@@ -63,6 +69,7 @@ constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
 constexpr int kRSegMinElems = kRSegBytes / 4;
 constexpr int kBlocksPerCU = 8;      // 32 wavefronts per CU
 constexpr int kPlanThreads = 1024;
+constexpr int kMaxEarlyExitRounds = 4096;   // bound on max_k (two launches per round)
 
 constexpr uint32_t kDraftBit = 1u << 30;
 constexpr uint32_t kGreedyBit = 1u << 29;
@@ -90,7 +97,10 @@ struct Header {
   int n_rows;
   int n_units;
   int n_resid;
-  int pad[60];
+  int n_rows3[3];     // early-exit rounds: rows listed for a round (three lists in rotation)
+  int n_res3[3];      // early-exit rounds: residual sweeps listed for a round
+  int n_alive3[3];    // early-exit rounds: requests deciding a position in the round
+  int pad[51];
 };
 
 struct Workspace {
@@ -101,6 +111,9 @@ struct Workspace {
   Partial* pt;         // [(K + B) * nseg]
   Partial* pd;         // [K * nseg]
   double* rp;          // [B * nrseg]
+  uint32_t* rows_r;    // [3][2B]    early-exit rounds: row descriptors
+  int* res_r;          // [3][B]     early-exit rounds: requests whose residual is swept
+  int* alive;          // [3][B]     early-exit rounds: requests deciding a position
 };
 
 struct Args {
@@ -121,6 +134,10 @@ struct Args {
   float* resid_out;
   float c_hi, c_lo;    // log2(e)/T split into two fp32 constants, c_lo > 0
   double c64, T64;
+  const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
+  const int* rowcount;       // number of rows in rowlist
+  int ee_round;              // early-exit round, -1 on the all-rows path
+  int max_k;                 // early-exit: bound on every num_draft[b]
   Workspace ws;
 };
 
@@ -438,15 +455,15 @@ __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
-  const int n_units = a.ws.hdr->n_units;
+  const int n_units = *a.rowcount * a.nseg;
   const Elem* tgt = static_cast<const Elem*>(a.target);
   const Elem* drf = static_cast<const Elem*>(a.draft);
-  uint32_t next = (gw < n_units) ? a.ws.rowdesc[gw / a.nseg] : 0u;
+  uint32_t next = (gw < n_units) ? a.rowlist[gw / a.nseg] : 0u;
   for (int u = gw; u < n_units; u += W) {
     const uint32_t desc = next;
     const int ri = u / a.nseg;
     const int seg = u - ri * a.nseg;
-    if (u + W < n_units) next = a.ws.rowdesc[(u + W) / a.nseg];
+    if (u + W < n_units) next = a.rowlist[(u + W) / a.nseg];
     const int row = (int)(desc & kRowMask);
     const bool is_draft = (desc & kDraftBit) != 0;
     const bool greedy = (desc & kGreedyBit) != 0;
@@ -463,9 +480,10 @@ __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
 
 // ------------------------------------------------------------------ row combines
 // One lane combines the nseg unit partials of one row.  Loads are issued in
-// groups of 8 so that they are in flight together; unit factors use the same
-// split-constant exp2 as the streaming kernels and accumulate in fp64.
-constexpr int kCombineGroup = 8;
+// groups of 16 so that they are in flight together (one group covers a
+// 262144-id bf16 row); unit factors use the same split-constant exp2 as the
+// streaming kernels and accumulate in fp64.
+constexpr int kCombineGroup = 16;
 
 __device__ void row_softmax(const Partial* P, int nseg, float c_hi, float c_lo, float& M,
                             double& S) {
@@ -719,13 +737,63 @@ __device__ __forceinline__ TargetW target_weights(const ReqInfo& R, const Args& 
   return w;
 }
 
+// Sum of [p - q]_+ over the ids [s0, s1) of one (target, draft) row pair, the
+// rejected id y excluded; one wavefront, result in every lane.
+template <class L, int U>
+__device__ __forceinline__ double resid_unit(const typename L::Elem* tp, const typename L::Elem* dp,
+                                             const ResidW& fw, int y, int s0, int s1, int lane) {
+  constexpr int E = L::E;
+  const int n = s1 - s0;
+  const int nchunk = n / E;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  auto chunk = [&](const typename L::Raw& rt, const typename L::Raw& rd, int id0) {
+    float vt[E], vd[E];
+    L::unpack(rt, vt);
+    L::unpack(rd, vd);
+    float r[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) r[e] = fw(vt[e], vd[e]);
+    if ((unsigned)(y - id0) < (unsigned)E) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (id0 + e == y) r[e] = 0.f;   // reject => p(y) < q(y) => [p - q]_+ is 0 at y
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += r[e];
+  };
+  constexpr int per_it = kWave * U;
+  const int nit = nchunk / per_it;
+  int c = lane;
+  for (int it = 0; it < nit; ++it, c += per_it) {
+    typename L::Raw rt[U], rd[U];
+#pragma unroll
+    for (int jj = 0; jj < U; ++jj) {
+      rt[jj] = L::stream(tp + s0 + (size_t)(c + jj * kWave) * E);
+      rd[jj] = L::stream(dp + s0 + (size_t)(c + jj * kWave) * E);
+    }
+#pragma unroll
+    for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
+  }
+  for (; c < nchunk; c += kWave)
+    chunk(L::stream(tp + s0 + (size_t)c * E), L::stream(dp + s0 + (size_t)c * E), s0 + c * E);
+  const int tail0 = nchunk * E;
+  if (lane < n - tail0) {
+    const int v = s0 + tail0 + lane;
+    if (v != y) acc[0] += fw(L::one(tp + v), L::one(dp + v));
+  }
+  float sl = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sl += acc[e];
+  return wave_sum((double)sl);
+}
+
 // ------------------------------------------------------------------ k_resid
 // Persistent grid; one wavefront per residual unit (rseg ids of one row pair).
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
   using Elem = typename L::Elem;
-  constexpr int E = L::E;
-  constexpr int U = 4;
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
@@ -752,51 +820,7 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
     }
     const int s0 = seg * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
-    const int n = s1 - s0;
-    const int nchunk = n / E;
-    const int y = R.y;
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    auto chunk = [&](const typename L::Raw& rt, const typename L::Raw& rd, int id0) {
-      float vt[E], vd[E];
-      L::unpack(rt, vt);
-      L::unpack(rd, vd);
-      float r[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) r[e] = fw(vt[e], vd[e]);
-      if ((unsigned)(y - id0) < (unsigned)E) {
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (id0 + e == y) r[e] = 0.f;   // reject => p(y) < q(y) => [p - q]_+ is 0 at y
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += r[e];
-    };
-    constexpr int per_it = kWave * U;
-    const int nit = nchunk / per_it;
-    int c = lane;
-    for (int it = 0; it < nit; ++it, c += per_it) {
-      typename L::Raw rt[U], rd[U];
-#pragma unroll
-      for (int jj = 0; jj < U; ++jj) {
-        rt[jj] = L::stream(tp + s0 + (size_t)(c + jj * kWave) * E);
-        rd[jj] = L::stream(dp + s0 + (size_t)(c + jj * kWave) * E);
-      }
-#pragma unroll
-      for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
-    }
-    for (; c < nchunk; c += kWave)
-      chunk(L::stream(tp + s0 + (size_t)c * E), L::stream(dp + s0 + (size_t)c * E), s0 + c * E);
-    const int tail0 = nchunk * E;
-    if (lane < n - tail0) {
-      const int v = s0 + tail0 + lane;
-      if (v != y) acc[0] += fw(L::one(tp + v), L::one(dp + v));
-    }
-    float sl = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) sl += acc[e];
-    const double tot = wave_sum((double)sl);
+    const double tot = resid_unit<L, 4>(tp, dp, fw, R.y, s0, s1, lane);
     if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
   }
 }
@@ -1014,6 +1038,291 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
   }
 }
 
+// ------------------------------------------------------------------ early exit
+// Left-to-right verification that reads only the rows up to each request's
+// cut.  Round j is two launches: k_round streams the position-j rows of every
+// request still undecided (and the residual row pairs of the requests cut at
+// j - 1), then k_decide_round decides position j of those requests and lists
+// the kept ones, their next rows and the new residual sweeps for round j + 1.
+// Lists rotate over three buffers; k_round of round j clears the counts of
+// the list that k_decide_round of round j fills.  No kernel waits on another
+// wavefront: every hand-over is a kernel boundary.
+
+// One workgroup: offsets as in k_plan, every output set to -1 (slots no round
+// reaches keep it), round 0 lists every request with its position-0 rows.
+__global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  __shared__ long long s_wk[kPlanWaves];
+  __shared__ long long s_wr[kPlanWaves];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
+  if (tid == 0) s_bad = 0;
+  for (long long i = tid; i < (long long)a.K + a.B; i += kPlanThreads) a.out[i] = -1;
+  for (long long i = tid; i < a.K; i += kPlanThreads) {
+    if (a.p_out) a.p_out[i] = -1.f;
+    if (a.q_out) a.q_out[i] = -1.f;
+  }
+  for (int i = tid; i < a.B; i += kPlanThreads) {
+    a.acc_len[i] = -1;
+    if (a.resid_out) a.resid_out[i] = -1.f;
+  }
+  __syncthreads();
+  long long carry_k = 0, carry_r = 0;
+  for (int base = 0; base < a.B; base += kPlanThreads) {
+    const int b = base + tid;
+    long long k = 0;
+    int g = 1;
+    if (b < a.B) {
+      int kk = a.num_draft[b];
+      if (kk < 0 || kk > a.K || kk > a.max_k) {
+        s_bad = 1;
+        kk = 0;
+      }
+      k = kk;
+      g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
+    }
+    const bool pair = (b < a.B) && !g && k > 0;
+    const long long nr = (b < a.B) ? (pair ? 2 : 1) : 0;   // rows read in round 0
+    const long long ik = wave_incl_scan_ll(k, lane);
+    const long long ir = wave_incl_scan_ll(nr, lane);
+    if (lane == kWave - 1) {
+      s_wk[wv] = ik;
+      s_wr[wv] = ir;
+    }
+    __syncthreads();
+    long long pk = 0, pr = 0, tot_k = 0, tot_r = 0;
+    for (int q = 0; q < kPlanWaves; ++q) {
+      if (q < wv) {
+        pk += s_wk[q];
+        pr += s_wr[q];
+      }
+      tot_k += s_wk[q];
+      tot_r += s_wr[q];
+    }
+    const long long off = carry_k + pk + ik - k;
+    const long long roff = carry_r + pr + ir - nr;
+    if (b < a.B) {
+      ReqInfo r;
+      r.off = (int)off;
+      r.k = (int)k;
+      r.greedy = g;
+      r.a = 0;
+      r.kind = KIND_NONE;
+      r.y = -1;
+      r.trow = -1;
+      r.drow = -1;
+      r.Mp = r.Mq = 0.f;
+      r.pad0 = r.pad1 = 0;
+      r.Sp = r.Sq = 0.0;
+      a.ws.req[b] = r;
+      a.ws.alive[b] = b;
+      const long long trow = off + b;
+      if (roff < 2ll * a.B && trow < (long long)a.K + a.B)
+        a.ws.rows_r[roff] = (uint32_t)trow | (g ? kGreedyBit : 0u);
+      if (pair && roff + 1 < 2ll * a.B && off < a.K)
+        a.ws.rows_r[roff + 1] = (uint32_t)off | kDraftBit;
+    }
+    carry_k += tot_k;
+    carry_r += tot_r;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const bool bad = s_bad != 0 || carry_k != a.K;
+    Header* h = a.ws.hdr;
+    h->error = bad ? 1 : 0;
+    h->n_resid = 0;
+    h->n_rows3[0] = bad ? 0 : (int)carry_r;
+    h->n_res3[0] = 0;
+    h->n_alive3[0] = bad ? 0 : a.B;
+    h->n_rows3[1] = 0;
+    h->n_res3[1] = 0;
+    h->n_alive3[1] = 0;
+    h->n_rows = 0;
+    h->n_units = 0;
+  }
+}
+
+// Decision of position j of request b by one wavefront.  Lane 0 combines the
+// target row and lane 1 the draft row with the per-row combines of k_decide,
+// so both paths see the same statistics bit for bit.
+template <class L>
+__device__ __forceinline__ void decide_position(const Args& a, int b, int j, int nxt, int lane) {
+  Header* hdr = a.ws.hdr;
+  const ReqInfo R = a.ws.req[b];
+  const int k = R.k;
+  const bool g = R.greedy != 0;
+  const int trow = R.off + b + j;
+  const int drow = R.off + j;
+  const int nseg = a.nseg;
+  if (j == 0 && !g) {
+    // a stochastic request with a draft token outside [0, V) reports -1
+    // everywhere, as on the all-rows path: all its tokens are tested up front
+    bool bad = false;
+    for (int i = lane; i < k; i += kWave) {
+      const int y = a.tokens[R.off + i];
+      bad |= (y < 0 || y >= a.V);
+    }
+    if (__any(bad)) return;             // outputs keep the -1 written by the plan
+  }
+  // loads that depend only on the request are issued before the row combines
+  int y = 0;
+  float zy = 0.f, dy = 0.f, u = 0.f;
+  if (lane == 0 && j < k) {
+    y = a.tokens[drow];
+    if (!g) {
+      u = a.u_accept[drow];
+      if (y >= 0 && y < a.V) {          // checked for every token in round 0
+        zy = logit_at<L>(a.target, trow, a.tld, y);
+        dy = logit_at<L>(a.draft, drow, a.dld, y);
+      }
+    }
+  }
+  const bool draft_row = !g && j < k;
+  float M = 0.f;
+  double S = 0.0;
+  int amax = INT_MAX;
+  if (lane == 0 && g) {
+    row_argmax(a.ws.pt + (int64_t)trow * nseg, nseg, amax);
+  } else if (lane == 0 || (lane == 1 && draft_row)) {
+    const Partial* P = (lane == 0) ? a.ws.pt + (int64_t)trow * nseg
+                                   : a.ws.pd + (int64_t)drow * nseg;
+    row_softmax(P, nseg, a.c_hi, a.c_lo, M, S);
+  }
+  const float Mq = __shfl(M, 1);
+  const double Sq = __shfl(S, 1);
+  M = __shfl(M, 0);
+  S = __shfl(S, 0);
+  amax = __shfl(amax, 0);
+  if (j == k) {                         // every draft kept: the final token
+    if (g) {
+      if (lane == 0) {
+        a.acc_len[b] = k;
+        a.out[trow] = (amax == INT_MAX) ? -1 : amax;
+      }
+    } else if (lane == 0) {             // drawn by k_finalize after the last round
+      ReqInfo Wr = R;
+      Wr.a = k;
+      Wr.trow = trow;
+      Wr.kind = KIND_BONUS;
+      Wr.Mp = M;
+      Wr.Sp = S;
+      a.acc_len[b] = k;
+      a.ws.req[b] = Wr;
+    }
+    return;
+  }
+  if (lane != 0) return;
+  bool rej;
+  if (g) {
+    rej = (y != amax);
+  } else {
+    const double py = exp(((double)zy - (double)M) / a.T64) / S;
+    const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
+    rej = !((double)u * qy < py);
+    if (a.p_out) a.p_out[drow] = (float)py;
+    if (a.q_out) a.q_out[drow] = (float)qy;
+  }
+  if (!rej) {                           // keep y_j, list position j + 1
+    a.out[trow] = y;
+    const int ia = atomicAdd(&hdr->n_alive3[nxt], 1);
+    a.ws.alive[(int64_t)nxt * a.B + ia] = b;
+    const bool pair = !g && j + 1 < k;
+    const int ir = atomicAdd(&hdr->n_rows3[nxt], pair ? 2 : 1);
+    uint32_t* rows = a.ws.rows_r + (int64_t)nxt * 2 * a.B;
+    rows[ir] = (uint32_t)(trow + 1) | (g ? kGreedyBit : 0u);
+    if (pair) rows[ir + 1] = (uint32_t)(drow + 1) | kDraftBit;
+  } else {                              // cut at j
+    a.acc_len[b] = j;
+    if (g) {
+      a.out[trow] = (amax == INT_MAX) ? -1 : amax;
+    } else {                            // pair swept in round j + 1, drawn by k_finalize
+      ReqInfo Wr = R;
+      Wr.a = j;
+      Wr.trow = trow;
+      Wr.drow = drow;
+      Wr.y = y;
+      Wr.kind = KIND_RESID;
+      Wr.Mp = M;
+      Wr.Sp = S;
+      Wr.Mq = Mq;
+      Wr.Sq = Sq;
+      a.ws.req[b] = Wr;
+      const int ir = atomicAdd(&hdr->n_res3[nxt], 1);
+      a.ws.res_r[(int64_t)nxt * a.B + ir] = b;
+    }
+  }
+}
+
+// Round j (a.ee_round), streaming half: persistent grid over the round's
+// units, row units first, then residual units.
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_round(Args a) {
+  using Elem = typename L::Elem;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int W = gridDim.x * kWavesPerBlock;
+  const int j = a.ee_round;
+  const int cur = j % 3, nxt = (j + 1) % 3;
+  Header* hdr = a.ws.hdr;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    // the lists k_decide_round of this round fills; round j - 2 read them
+    hdr->n_rows3[nxt] = 0;
+    hdr->n_res3[nxt] = 0;
+    hdr->n_alive3[nxt] = 0;
+  }
+  const int n_s = hdr->n_rows3[cur] * a.nseg;
+  const int n_units = n_s + hdr->n_res3[cur] * a.nrseg;
+  const uint32_t* rows = a.ws.rows_r + (int64_t)cur * 2 * a.B;
+  const int* res = a.ws.res_r + (int64_t)cur * a.B;
+  const Elem* tgt = static_cast<const Elem*>(a.target);
+  const Elem* drf = static_cast<const Elem*>(a.draft);
+  for (int u = gw; u < n_units; u += W) {
+    if (u < n_s) {
+      const int ri = u / a.nseg;
+      const int seg = u - ri * a.nseg;
+      const uint32_t desc = rows[ri];
+      const int row = (int)(desc & kRowMask);
+      const bool is_draft = (desc & kDraftBit) != 0;
+      const int s0 = seg * a.seg;
+      const int s1 = min(s0 + a.seg, a.V);
+      const Elem* base = is_draft ? drf + (int64_t)row * a.dld : tgt + (int64_t)row * a.tld;
+      Partial* out = (is_draft ? a.ws.pd : a.ws.pt) + (int64_t)row * a.nseg + seg;
+      if (desc & kGreedyBit)
+        argmax_unit<L>(base, s0, s1, lane, out);
+      else
+        softmax_unit<L>(base, s0, s1, lane, a, out);
+    } else {                            // residual unit of a request cut at j - 1
+      const int v = u - n_s;
+      const int ri = v / a.nrseg;
+      const int seg = v - ri * a.nrseg;
+      const int b = res[ri];
+      const ReqInfo R = a.ws.req[b];
+      const Elem* tp = tgt + (int64_t)R.trow * a.tld;
+      const Elem* dp = drf + (int64_t)R.drow * a.dld;
+      const int s0 = seg * a.rseg;
+      const int s1 = min(s0 + a.rseg, a.V);
+      const double tot = resid_unit<L, kUnroll>(tp, dp, resid_weights(R, a), R.y, s0, s1, lane);
+      if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
+    }
+  }
+}
+
+// Round j, deciding half: one wavefront per request whose position-j rows the
+// round streamed.
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_decide_round(Args a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int W = gridDim.x * kWavesPerBlock;
+  const int j = a.ee_round;
+  const int cur = j % 3, nxt = (j + 1) % 3;
+  const int nal = a.ws.hdr->n_alive3[cur];
+  for (int w = gw; w < nal; w += W)
+    decide_position<L>(a, a.ws.alive[(int64_t)cur * a.B + w], j, nxt, lane);
+}
+
 // ------------------------------------------------------------------ acceptance statistics
 // One workgroup: LDS histograms of accepted and proposed lengths over
 // [0, max_pos] (larger values fold into the top bin, which keeps every
@@ -1069,7 +1378,8 @@ __global__ __launch_bounds__(kStatsThreads) void k_accept_stats(const int* acc, 
 size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
 
 struct Sizes {
-  size_t off_hdr, off_req, off_rowdesc, off_resid, off_pt, off_pd, off_rp, total;
+  size_t off_hdr, off_req, off_rowdesc, off_resid, off_pt, off_pd, off_rp, off_rows_r, off_res_r,
+      off_alive, total;
 };
 
 bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
@@ -1086,6 +1396,9 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)((K + B) * nseg), 256);
   z->off_pd = o; o = align_up(o + sizeof(Partial) * (size_t)(K * nseg), 256);
   z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nrseg), 256);
+  z->off_rows_r = o; o = align_up(o + 4 * (size_t)(6 * B), 256);
+  z->off_res_r = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
+  z->off_alive = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
   z->total = o + 256;   // slack for aligning the caller's pointer
   return true;
 }
@@ -1156,12 +1469,33 @@ void launch_all(const Args& a, hipStream_t st, int dev, bool sample) {
   }
 }
 
+template <class L>
+void launch_early_exit(const Args& a, hipStream_t st, int dev, bool sample) {
+  static std::atomic<int> occ_round[64];
+  const long long cus = cu_count(dev);
+  const long long units_max = 2ll * a.B * a.nseg + (long long)a.B * a.nrseg;
+  const long long cap = cus * resident_blocks(occ_round, k_round<L>, dev);
+  const int grid = (int)std::max(1ll, std::min(cap, (units_max + kWavesPerBlock - 1) / kWavesPerBlock));
+  const int grid_dec = (int)std::max(1ll, std::min(cus * kBlocksPerCU, ((long long)a.B + kWavesPerBlock - 1) / kWavesPerBlock));
+  k_plan_ee<<<1, kPlanThreads, 0, st>>>(a);
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
+  for (int j = 0; j <= a.max_k; ++j) {
+    Args r = a;
+    r.ee_round = j;
+    k_round<L><<<grid, kBlock, 0, st>>>(r);
+    k_decide_round<L><<<grid_dec, kBlock, 0, st>>>(r);
+  }
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
+  if (sample) k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
+}
+
 int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t* gmask,
             const float* u_accept, const float* u_final, int32_t* acc_len, int32_t* out,
             float* p_out, float* q_out, float* resid_out, void* ws, size_t ws_bytes,
-            void* stream) {
+            void* stream, bool early_exit, int max_k) {
   // ---- host-side checks: nothing below touches the GPU until they pass
   if (!bt) return SV_ERR_INVALID_ARG;
+  if (early_exit && (max_k < 0 || max_k > kMaxEarlyExitRounds)) return SV_ERR_INVALID_ARG;
   const long long B = bt->B, K = bt->K, V = bt->V;
   Sizes z;
   if (!compute_sizes(B, K, V, &z)) return SV_ERR_INVALID_ARG;
@@ -1223,6 +1557,13 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
   a.ws.pd = reinterpret_cast<Partial*>(wb + z.off_pd);
   a.ws.rp = reinterpret_cast<double*>(wb + z.off_rp);
+  a.ws.rows_r = reinterpret_cast<uint32_t*>(wb + z.off_rows_r);
+  a.ws.res_r = reinterpret_cast<int*>(wb + z.off_res_r);
+  a.ws.alive = reinterpret_cast<int*>(wb + z.off_alive);
+  a.rowlist = a.ws.rowdesc;
+  a.rowcount = &a.ws.hdr->n_rows;
+  a.ee_round = -1;
+  a.max_k = max_k;
 
   bool vec = ((uintptr_t)bt->target % 16 == 0) && ((bt->target_ld * es) % 16 == 0);
   if (need_draft) vec = vec && ((uintptr_t)bt->draft % 16 == 0) && ((bt->draft_ld * es) % 16 == 0);
@@ -1232,7 +1573,15 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   (void)hipGetLastError();   // clear a stale error from earlier unrelated calls
-  if (bt->dtype == SV_F32) {
+  if (early_exit) {
+    if (bt->dtype == SV_F32) {
+      if (vec) launch_early_exit<F32>(a, st, dev, sample);
+      else launch_early_exit<Scalar<F32>>(a, st, dev, sample);
+    } else {
+      if (vec) launch_early_exit<BF16>(a, st, dev, sample);
+      else launch_early_exit<Scalar<BF16>>(a, st, dev, sample);
+    }
+  } else if (bt->dtype == SV_F32) {
     if (vec) launch_all<F32>(a, st, dev, sample);
     else launch_all<Scalar<F32>>(a, st, dev, sample);
   } else {
@@ -1266,7 +1615,15 @@ extern "C" int32_t spec_verify_greedy(const sv_batch_t* batch, int32_t* accepted
                                       int32_t* out_tokens, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   return run(batch, false, 1.f, nullptr, nullptr, nullptr, accepted_len, out_tokens, nullptr,
-             nullptr, nullptr, workspace, workspace_bytes, stream);
+             nullptr, nullptr, workspace, workspace_bytes, stream, false, 0);
+}
+
+extern "C" int32_t spec_verify_greedy_early_exit(const sv_batch_t* batch, int32_t max_k,
+                                                 int32_t* accepted_len, int32_t* out_tokens,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+  return run(batch, false, 1.f, nullptr, nullptr, nullptr, accepted_len, out_tokens, nullptr,
+             nullptr, nullptr, workspace, workspace_bytes, stream, true, max_k);
 }
 
 extern "C" int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
@@ -1276,7 +1633,18 @@ extern "C" int32_t spec_verify_sample(const sv_batch_t* batch, float temperature
                                       float* resid_mass, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   return run(batch, true, temperature, greedy_mask, u_accept, u_final, accepted_len, out_tokens,
-             p_draft, q_draft, resid_mass, workspace, workspace_bytes, stream);
+             p_draft, q_draft, resid_mass, workspace, workspace_bytes, stream, false, 0);
+}
+
+extern "C" int32_t spec_verify_sample_early_exit(const sv_batch_t* batch, int32_t max_k,
+                                                 float temperature, const uint8_t* greedy_mask,
+                                                 const float* u_accept, const float* u_final,
+                                                 int32_t* accepted_len, int32_t* out_tokens,
+                                                 float* p_draft, float* q_draft, float* resid_mass,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+  return run(batch, true, temperature, greedy_mask, u_accept, u_final, accepted_len, out_tokens,
+             p_draft, q_draft, resid_mass, workspace, workspace_bytes, stream, true, max_k);
 }
 
 extern "C" int32_t spec_verify_accept_stats(const int32_t* accepted_len, const int32_t* num_draft,

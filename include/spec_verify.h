@@ -126,6 +126,32 @@ int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
                            float* p_draft, float* q_draft, float* resid_mass,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Left-to-right verification with early exit (chzhyang section 1 and the vLLM
+ * blog, "Core idea of speculative decoding": drafts after the first rejection
+ * are discarded, so their rows need not be read).  Same results as
+ * spec_verify_greedy / spec_verify_sample for accepted_len, out_tokens and
+ * resid_mass, bit for bit, but reads only the rows up to each request's cut:
+ * position j of every request still alive is verified in round j, one round
+ * per two kernel launches.
+ *   max_k     bound on every num_draft[b], 0 <= max_k <= 4096; the call runs
+ *             max_k + 1 rounds.  A request with num_draft[b] > max_k is a
+ *             device-side input error (every output -1, as for an
+ *             inconsistent num_draft).
+ *   p_draft, q_draft  p(y_i), q(y_i) of the positions actually tested (every
+ *             position up to and including the cut); -1 for later positions,
+ *             for greedy requests and for requests with an invalid token.
+ * Other arguments, the workspace size and errors as for the functions above. */
+int32_t spec_verify_greedy_early_exit(const sv_batch_t* batch, int32_t max_k,
+                                      int32_t* accepted_len, int32_t* out_tokens,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+int32_t spec_verify_sample_early_exit(const sv_batch_t* batch, int32_t max_k,
+                                      float temperature, const uint8_t* greedy_mask,
+                                      const float* u_accept, const float* u_final,
+                                      int32_t* accepted_len, int32_t* out_tokens,
+                                      float* p_draft, float* q_draft, float* resid_mass,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Acceptance statistics of verification outcomes, the signals of the vLLM blog
  * post "speculative-decoding-amd-gpus" ("Monitor acceptance behavior", and the
  * per-position columns of its Appendix tables).  Inputs are the accepted_len
@@ -145,8 +171,8 @@ int32_t spec_verify_accept_stats(const int32_t* accepted_len, const int32_t* num
 
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
- * before and ev_end just after the row-statistics kernel, on the call's
- * stream.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
+ * before and ev_end just after the row-statistics kernel (for the early-exit
+ * entry points: around all rounds), on the call's stream.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
 int32_t spec_verify_set_profile_events(void* ev_begin, void* ev_end);
 
 #ifdef __cplusplus

@@ -169,3 +169,26 @@ def test_accept_stats_host_validation(sv):
     assert f(FAKE, FAKE, 0, 3, FAKE, None) == INV
     assert f(FAKE, FAKE, 4, 0, FAKE, None) == INV
     assert f(FAKE, FAKE, 4, 4097, FAKE, None) == INV
+
+
+def test_early_exit_host_validation(sv):
+    INV, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_workspace_bytes(4, 8, 1000)
+    g = sv._lib.spec_verify_greedy_early_exit
+    s = sv._lib.spec_verify_sample_early_exit
+
+    def smp(bt, max_k, T=1.0, wsb=need, ua=FAKE):
+        return s(ctypes.byref(bt), max_k, ctypes.c_float(T), None, ua, FAKE, FAKE, FAKE, None,
+                 None, None, FAKE, wsb, None)
+
+    for mk in (-1, 4097, -(1 << 30)):
+        assert g(ctypes.byref(_batch(sv)), mk, FAKE, FAKE, FAKE, need, None) == INV, mk
+        assert smp(_batch(sv), mk) == INV, mk
+    assert g(None, 4, FAKE, FAKE, FAKE, need, None) == INV
+    assert g(ctypes.byref(_batch(sv, B=0)), 4, FAKE, FAKE, FAKE, need, None) == INV
+    assert g(ctypes.byref(_batch(sv)), 4, FAKE, None, FAKE, need, None) == INV
+    assert g(ctypes.byref(_batch(sv)), 4, FAKE, FAKE, FAKE, need - 1, None) == WS
+    assert smp(_batch(sv), 4, T=0.0) == INV
+    assert smp(_batch(sv), 4, ua=None) == INV
+    assert smp(_batch(sv), 4, wsb=need - 1) == WS
+    assert smp(_batch(sv, draft=None), 4) == INV

@@ -1,0 +1,181 @@
+"""Early-exit verification (rows read only up to each request's cut) against the
+fp64 oracle and against the all-rows entry points (needs the GPU).
+
+Accepted lengths, committed tokens and residual masses follow the oracle's
+rule of tests/parity.py; p(y), q(y) are compared at the tested positions
+(every position up to and including the cut) and must be -1 elsewhere.
+Against the all-rows path the outputs are bit-identical.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.parity import compare, run_hip, run_oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _tested_positions(batch, acc):
+    """Boolean [K]: draft position i of request b was tested (stochastic, i <= a_b)."""
+    nd = batch.num_draft.astype(np.int64)
+    mask = np.zeros(int(nd.sum()), bool)
+    off = np.concatenate([[0], np.cumsum(nd)])
+    for b in range(batch.B):
+        if batch.temperature is None or batch.greedy[b] or acc[b] < 0:
+            continue
+        n = min(int(acc[b]) + 1, int(nd[b]))
+        mask[off[b]:off[b] + n] = True
+    return mask
+
+
+def _oracle_as_tested(batch, got, ref):
+    """The oracle's p, q restricted to the positions the early-exit call tested."""
+    if ref.get("p_draft") is None or got.get("p_draft") is None:
+        return ref
+    r = dict(ref)
+    mask = _tested_positions(batch, got["accepted_len"])
+    r["p_draft"] = np.where(mask, ref["p_draft"], -1.0)
+    r["q_draft"] = np.where(mask, ref["q_draft"], -1.0)
+    return r
+
+
+def _assert_same_as_all_rows(batch, got, full, label):
+    assert np.array_equal(got["accepted_len"], full["accepted_len"]), label
+    assert np.array_equal(got["out_tokens"], full["out_tokens"]), label
+    if got.get("resid_mass") is not None:
+        assert np.array_equal(got["resid_mass"], full["resid_mass"]), label
+        mask = _tested_positions(batch, got["accepted_len"])
+        for name in ("p_draft", "q_draft"):
+            assert np.array_equal(got[name][mask], full[name][mask]), (label, name)
+            assert np.all(got[name][~mask] == -1.0), (label, name)
+
+
+CASES = [
+    ("c1_full", 1, {}, 0),
+    ("c2_full", 2, {}, 0),
+    ("c3_f32_V40003", 3, dict(B=8, V=40003), 0),
+    ("c4_bf16_V151936", 4, dict(B=3), 3),
+    ("c5_mixed_V70001", 5, dict(B=24, V=70001), 0),
+    ("c5_strided_scalar", 5, dict(B=12, V=9999, target_ld=10001), 1),
+    ("k0_all_mixed", 5, dict(B=16, V=20000, k=0), 0),
+    ("c4_tiny_vocab", 4, dict(B=64, V=64), 0),
+    ("c3_vocab_1", 3, dict(B=4, V=1, k=2), 0),
+    ("c5_many_requests", 5, dict(B=2100, V=300), 2),
+    ("c2_greedy_odd_V", 2, dict(B=40, V=33333), 5),
+]
+
+
+@pytest.mark.parametrize("label,cfg,kw,extra", CASES, ids=[c[0] for c in CASES])
+def test_early_exit_parity(label, cfg, kw, extra):
+    """max_k = the largest k_b plus `extra` empty rounds."""
+    _log(f"[early-exit] {label} cfg={cfg} {kw} extra={extra}")
+    batch = synth.make_batch(cfg, DEV, **kw)
+    max_k = int(batch.num_draft.max(initial=0)) + extra
+    got = run_hip(batch, max_k=max_k)
+    ref = run_oracle(batch)
+    near = compare(batch, got, _oracle_as_tested(batch, got, ref), label)
+    full = run_hip(batch)
+    _assert_same_as_all_rows(batch, got, full, label)
+    n_stoch = int((batch.greedy == 0).sum()) if batch.temperature is not None else 0
+    _log(f"[early-exit] {label}: B={batch.B} K={batch.K} max_k={max_k} near_ties={near}")
+    assert near <= max(1, n_stoch // 100)
+
+
+def test_early_exit_count_above_bound_is_an_input_error():
+    import draft_token_verification_row_amd as sv
+    batch = synth.make_batch(5, DEV, B=10, V=5000)
+    nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=DEV)
+    gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=DEV)
+    kmax = int(batch.num_draft.max())
+    r = sv.spec_verify_sample(batch.target, batch.draft, batch.tokens, nd, batch.temperature,
+                              batch.u_accept, batch.u_final, greedy_mask=gm, max_k=kmax - 1)
+    torch.cuda.synchronize()
+    assert torch.all(r["accepted_len"] == -1) and torch.all(r["out_tokens"] == -1)
+    assert torch.all(r["p_draft"] == -1) and torch.all(r["resid_mass"] == -1)
+    # the same workspace then serves a valid call
+    r = sv.spec_verify_sample(batch.target, batch.draft, batch.tokens, nd, batch.temperature,
+                              batch.u_accept, batch.u_final, greedy_mask=gm, max_k=kmax)
+    torch.cuda.synchronize()
+    assert torch.all(r["accepted_len"] >= 0)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_greedy(batch.target, batch.tokens, nd, max_k=-1)
+    with pytest.raises(sv.SpecVerifyError):
+        sv.spec_verify_greedy(batch.target, batch.tokens, nd, max_k=4097)
+
+
+def test_early_exit_invalid_token_marks_only_its_request():
+    import draft_token_verification_row_amd as sv
+    batch = synth.make_batch(5, DEV, B=10, V=5000)
+    nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=DEV)
+    gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=DEV)
+    cand = np.flatnonzero((batch.greedy == 0) & (batch.num_draft > 1))
+    b0 = int(cand[0])
+    off = batch.offsets
+    toks = batch.tokens.clone()
+    toks[int(off[b0]) + int(batch.num_draft[b0]) - 1] = -3     # last draft: past any cut
+    r = sv.spec_verify_sample(batch.target, batch.draft, toks, nd, batch.temperature,
+                              batch.u_accept, batch.u_final, greedy_mask=gm,
+                              max_k=int(batch.num_draft.max()))
+    torch.cuda.synchronize()
+    acc = r["accepted_len"].cpu().numpy()
+    assert acc[b0] == -1
+    sl = slice(int(off[b0]) + b0, int(off[b0]) + b0 + int(batch.num_draft[b0]) + 1)
+    assert np.all(r["out_tokens"].cpu().numpy()[sl] == -1)
+    dsl = slice(int(off[b0]), int(off[b0]) + int(batch.num_draft[b0]))
+    assert np.all(r["p_draft"].cpu().numpy()[dsl] == -1)
+    good = synth.select_requests(batch, [b for b in range(batch.B) if b != b0], device=DEV)
+    ref = run_oracle(good)
+    assert np.array_equal(np.delete(acc, b0), ref["accepted_len"])
+
+
+def test_early_exit_repeat_and_stream():
+    batch = synth.make_batch(5, DEV, B=64, V=30000)
+    mk = int(batch.num_draft.max())
+    a = run_hip(batch, max_k=mk)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_hip(batch, max_k=mk, stream=s)
+    s.synchronize()
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_early_exit_full_size(cfg):
+    """Full workload shape in the launch configuration the benchmark times:
+    bit-identical to the all-rows path, and a seeded sample against the oracle."""
+    _log(f"[early-exit full] cfg={cfg} generating")
+    batch = synth.make_batch(cfg, DEV)
+    torch.cuda.synchronize()
+    max_k = int(batch.num_draft.max())
+    _log(f"[early-exit full] cfg={cfg} B={batch.B} K={batch.K} V={batch.V} max_k={max_k}")
+    got = run_hip(batch, max_k=max_k)
+    full = run_hip(batch)
+    _assert_same_as_all_rows(batch, got, full, f"full cfg{cfg}")
+    rng = np.random.default_rng(2000 + cfg)
+    reqs = sorted(rng.choice(batch.B, size=min(12, batch.B), replace=False).tolist())
+    sub = synth.select_requests(batch, reqs, device="cpu")
+    ref = run_oracle(sub)
+    nd = batch.num_draft.astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(nd)])
+    sel = {"accepted_len": got["accepted_len"][reqs]}
+    sel["out_tokens"] = np.concatenate(
+        [got["out_tokens"][off[b] + b: off[b] + b + nd[b] + 1] for b in reqs])
+    if got.get("p_draft") is not None:
+        dr = np.concatenate([np.arange(off[b], off[b] + nd[b]) for b in reqs]).astype(np.int64)
+        sel["p_draft"] = got["p_draft"][dr]
+        sel["q_draft"] = got["q_draft"][dr]
+        sel["resid_mass"] = got["resid_mass"][reqs]
+    near = compare(sub, sel, _oracle_as_tested(sub, sel, ref), f"early-exit full cfg{cfg}")
+    _log(f"[early-exit full] cfg={cfg}: sampled {len(reqs)}, near_ties={near}")
+    assert near <= 1
