@@ -11,7 +11,9 @@ Prints ONE JSON line.  `value` = verified draft positions per second (sum of
 k_b per step / step time).  `roofline` describes the row-statistics kernel:
 algorithmic bytes (every logit row it must read, once) over its average
 duration measured with HIP events recorded around it on the call's stream.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload.
+`other_path` times the other entry point (early exit vs all rows) on the same
+batch.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -119,7 +121,8 @@ def main():
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps calls and exit without the JSON report (for rocprofv3)")
     ap.add_argument("--early-exit", action="store_true",
-                    help="time the early-exit entry points (rows read only up to each cut)")
+                    help="headline = the early-exit entry points (rows read only up to each cut); "
+                         "the all-rows path is then reported under other_path, and vice versa")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -160,30 +163,25 @@ def main():
     lib = sv._lib
     greedy_only = batch.temperature is None
     kmax = int(batch.num_draft.max()) if batch.K > 0 else 0
-    ee = args.early_exit
-    if greedy_only:
-        if ee:
-            def call():
-                return lib.spec_verify_greedy_early_exit(ctypes.byref(bt), kmax, acc.data_ptr(),
-                                                         out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
-        else:
-            def call():
-                return lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
-                                              ws.data_ptr(), ws_bytes, sh)
-    else:
+
+    def make_call(early_exit: bool):
+        if greedy_only:
+            if early_exit:
+                return lambda: lib.spec_verify_greedy_early_exit(
+                    ctypes.byref(bt), kmax, acc.data_ptr(), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+            return lambda: lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
+                                                  ws.data_ptr(), ws_bytes, sh)
         T = ctypes.c_float(batch.temperature)
         a_ptrs = (gm.data_ptr() if gm is not None else None, batch.u_accept.data_ptr(),
                   batch.u_final.data_ptr(), acc.data_ptr(), out.data_ptr(), pdr.data_ptr(),
                   qdr.data_ptr(), rm.data_ptr())
-        if ee:
-            def call():
-                return lib.spec_verify_sample_early_exit(ctypes.byref(bt), kmax, T, *a_ptrs,
-                                                         ws.data_ptr(), ws_bytes, sh)
-        else:
-            def call():
-                return lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes,
-                                              sh)
+        if early_exit:
+            return lambda: lib.spec_verify_sample_early_exit(ctypes.byref(bt), kmax, T, *a_ptrs,
+                                                             ws.data_ptr(), ws_bytes, sh)
+        return lambda: lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes, sh)
 
+    ee = args.early_exit
+    call = make_call(ee)
     for _ in range(args.warmup):
         assert call() == 0
     torch.cuda.synchronize()
@@ -195,42 +193,59 @@ def main():
         return
 
     hip = HipEvents()
-    ev_b = hip.create(args.steps)
-    ev_e = hip.create(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
-        call()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sv.spec_verify_set_profile_events(None, None)
-    stats_ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(args.steps)]
-    hip.destroy(ev_b + ev_e)
 
-    step_s = (t1 - t0) / args.steps
-    positions = int(batch.num_draft.sum())
+    def timed(fn, steps):
+        """Wall time per call over `steps` calls, and the mean of the HIP-event
+        interval the library records around its row-statistics launches."""
+        ev_b = hip.create(steps)
+        ev_e = hip.create(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sv.spec_verify_set_profile_events(None, None)
+        ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
+        hip.destroy(ev_b + ev_e)
+        return (t1 - t0) / steps, float(np.mean(ms)) / 1e3
+
     es = 4 if batch.dtype == "f32" else 2
-    stoch_draft_rows = 0 if greedy_only else int(batch.num_draft[batch.greedy == 0].sum())
-    rows = batch.K + batch.B + stoch_draft_rows
-    if ee:
-        # rows up to each request's cut: a_b + 1 target rows, min(a_b + 1, k_b) draft rows
+    k_np = batch.num_draft.astype(np.int64)
+    stoch = np.zeros(batch.B, bool) if greedy_only else (batch.greedy == 0)
+
+    def rows_read(early_exit: bool) -> int:
+        if not early_exit:      # every target row, the draft rows of stochastic requests
+            return batch.K + batch.B + int(k_np[stoch].sum())
+        # up to each cut: a_b + 1 target rows, min(a_b + 1, k_b) draft rows
         a_np = acc.cpu().numpy().astype(np.int64)
-        k_np = batch.num_draft.astype(np.int64)
-        stoch = np.zeros(batch.B, bool) if greedy_only else (batch.greedy == 0)
-        rows = int((a_np + 1).sum() + np.minimum(a_np + 1, k_np)[stoch].sum())
-    bytes_stats = rows * batch.V * es                 # every row the kernel must read, once
-    t_stats = float(np.mean(stats_ms)) / 1e3
+        return int((a_np + 1).sum() + np.minimum(a_np + 1, k_np)[stoch].sum())
+
+    step_s, t_stats = timed(call, args.steps)
+    positions = int(batch.num_draft.sum())
+    rows = rows_read(ee)
+    bytes_stats = rows * batch.V * es
     achieved = bytes_stats / t_stats / 1e9
+
+    # the other entry point on the same batch, for comparison
+    other = make_call(not ee)
+    for _ in range(max(args.warmup // 2, 2)):
+        assert other() == 0
+    o_step, o_t = timed(other, max(args.steps // 2, 5))
+    o_bytes = rows_read(not ee) * batch.V * es
+    call()                      # leave the headline path's outputs in acc/out
+    torch.cuda.synchronize()
 
     traffic = None
     if os.path.exists(TRAFFIC):
         with open(TRAFFIC) as f:
             tr = json.load(f)
-        entry = tr.get(batch.name)
+        entry = tr.get(batch.name if not ee else batch.name + "/early_exit")
         if entry and entry.get("source_hash") == kernel_source_hash():
             traffic = entry.get("hbm_bytes_per_launch")
 
+    path = lambda e: ("early exit (max_k = %d)" % kmax) if e else "all rows"
     res = {
         "metric": METRIC,
         "value": positions / step_s,
@@ -250,13 +265,13 @@ def main():
             "requests": ("greedy" if greedy_only else
                          f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
             "parallelism": "single GPU",
-            "path": "early exit (max_k = %d)" % kmax if ee else "all rows",
+            "path": path(ee),
         },
         "rows_per_s": (batch.K + batch.B) / step_s,
         "hbm_gbs_step": bytes_stats / step_s / 1e9,
         "hbm_frac_step": bytes_stats / step_s / 1e9 / PEAK_HBM_GBS,
         "roofline": {
-            "kernel": ("rounds: k_stats + k_decide_round per position" if ee
+            "kernel": ("rounds: k_round + k_decide_round per position" if ee
                        else "k_stats (row statistics)"),
             "bound": "hbm",
             "achieved": achieved,
@@ -266,6 +281,15 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_stats,
             "avg_kernel_ms": t_stats * 1e3,
+        },
+        "other_path": {
+            "path": path(not ee),
+            "value": positions / o_step,
+            "ms_per_step": o_step * 1e3,
+            "logit_bytes_read": o_bytes,
+            "hbm_gbs_step": o_bytes / o_step / 1e9,
+            "timed_interval_ms": o_t * 1e3,
+            "speedup_of_headline": o_step / step_s,
         },
     }
     st = sv.spec_verify_accept_stats(acc, nd, max(kmax, 1)).cpu().numpy()
