@@ -6,7 +6,8 @@ cpu_baseline leg may import it.  Shares no code with the HIP path.
 from .verify import (verify_batch, verify_request, tempered_softmax, lowest_argmax,
                      keeps_draft, positive_residual, inverse_cdf, widen_temperature)
 from .cost_model import time_per_token, expected_progress
+from .tree import tree_walk_greedy, tree_verify_batch
 
 __all__ = ["verify_batch", "verify_request", "tempered_softmax", "lowest_argmax",
            "keeps_draft", "positive_residual", "inverse_cdf", "widen_temperature",
-           "time_per_token", "expected_progress"]
+           "time_per_token", "expected_progress", "tree_walk_greedy", "tree_verify_batch"]

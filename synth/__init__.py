@@ -290,3 +290,156 @@ def as_numpy(batch: Batch) -> dict:
         num_draft=batch.num_draft.astype(np.int64), greedy=batch.greedy.astype(bool),
         temperature=batch.temperature,
         u_accept=batch.u_accept.cpu().numpy(), u_final=batch.u_final.cpu().numpy())
+
+
+# ---------------------------------------------------------------------------
+# Token trees (greedy tree verification).  Shapes only: the verification walk
+# is not computed here.
+#
+# Request b owns n_b nodes (node 0 = root, the last committed token) in
+# creation order, so every parent index is below its child's.  Shapes grow by
+# best-first expansion of random factorized scores: a candidate child of node
+# i at sibling rank r scores score(i) * w_i[r], with w_i a random Dirichlet
+# draw sorted descending (the shape of the candidate sets that chzhyang,
+# "Speculative Decoding: ...", section 5 DDTree describes; the scores here are
+# random numbers, not a drafter's marginals).  Target logits are N(0, sigma^2)
+# per node row.  Sibling tokens are distinct; with probability p_match one
+# child of a node carries the argmax of the node's target row (so walks go
+# deep), the other children random other ids.
+
+TREE_CONFIGS = {
+    1: dict(name="tree_tiny_v1000", B=3, nodes=(1, 12), V=1000, dtype="f32", sigma=2.0,
+            p_match=0.7, branch=3),
+    2: dict(name="ddtree_budget32_v151936", B=32, nodes=33, V=151936, dtype="bf16",
+            sigma=2.0, p_match=0.75, branch=4),
+}
+
+
+@dataclasses.dataclass
+class TreeBatch:
+    """One packed batch of token trees.  Tensors live on `device`."""
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    num_nodes: np.ndarray          # int32 [B] (host copy)
+    parent: torch.Tensor           # int32 [N], local parent index (root's entry -1)
+    tokens: torch.Tensor           # int32 [N]
+    target: torch.Tensor           # [N, V]
+
+    @property
+    def offsets(self) -> np.ndarray:
+        off = np.zeros(self.B + 1, dtype=np.int64)
+        np.cumsum(self.num_nodes, out=off[1:])
+        return off
+
+    def to(self, device) -> "TreeBatch":
+        return dataclasses.replace(self, parent=self.parent.to(device),
+                                   tokens=self.tokens.to(device),
+                                   target=self.target.to(device))
+
+
+def _tree_shape(n: int, branch: int, rng: np.random.Generator) -> np.ndarray:
+    import heapq
+    parent = np.full(n, -1, dtype=np.int64)
+    score = np.zeros(n)
+    score[0] = 1.0
+    heap = []
+
+    def push_children(i):
+        w = np.sort(rng.dirichlet(np.ones(branch)))[::-1]
+        for r in range(branch):
+            heapq.heappush(heap, (-score[i] * w[r], int(rng.integers(1 << 30)), i))
+
+    push_children(0)
+    for i in range(1, n):
+        s, _, p = heapq.heappop(heap)
+        parent[i] = p
+        score[i] = -s
+        push_children(i)
+    return parent
+
+
+def make_tree_batch(cfg_id: int, device="cpu", *, B: Optional[int] = None,
+                    V: Optional[int] = None, nodes=None, seed: Optional[int] = None,
+                    dtype: Optional[str] = None, p_match: Optional[float] = None) -> TreeBatch:
+    cfg = TREE_CONFIGS[cfg_id]
+    B = cfg["B"] if B is None else B
+    V = cfg["V"] if V is None else V
+    nodes = cfg["nodes"] if nodes is None else nodes
+    dt = cfg["dtype"] if dtype is None else dtype
+    pm = cfg["p_match"] if p_match is None else p_match
+    ss = np.random.SeedSequence(BASE_SEED + 100 + cfg_id if seed is None else seed)
+    s_shape, s_target, s_tok = ss.spawn(3)
+    rng = np.random.default_rng(s_shape)
+    if isinstance(nodes, tuple):
+        num_nodes = rng.integers(nodes[0], nodes[1] + 1, size=B).astype(np.int32)
+    else:
+        num_nodes = np.full(B, int(nodes), dtype=np.int32)
+    N = int(num_nodes.sum())
+    parent = np.concatenate([_tree_shape(int(n), cfg["branch"], rng) for n in num_nodes]) \
+        if N else np.zeros(0, np.int64)
+    g_t = _torch_gen(s_target, device)
+    target = (torch.randn((N, V), generator=g_t, device=device, dtype=torch.float32)
+              * cfg["sigma"]).to(TORCH_DTYPE[dt])
+    amax = torch.argmax(target.to(torch.float32), dim=1).cpu().numpy() if N else np.zeros(0)
+    rt = np.random.default_rng(s_tok)
+    tokens = np.zeros(N, dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(num_nodes)]).astype(np.int64)
+    for b in range(B):
+        s, n = int(off[b]), int(num_nodes[b])
+        tokens[s] = rt.integers(0, V)                       # root: not verified
+        for i in range(n):
+            kids = [c for c in range(i + 1, n) if parent[s + c] == i]
+            if not kids:
+                continue
+            used = set()
+            if rt.random() < pm and V > len(kids):
+                tokens[s + kids[0]] = amax[s + i]
+                used.add(int(amax[s + i]))
+                kids = kids[1:]
+            banned = {int(amax[s + i])}
+            for c in kids:
+                while True:
+                    t = int(rt.integers(0, V))
+                    if t not in used and (t not in banned or V <= len(used) + 1):
+                        break
+                tokens[s + c] = t
+                used.add(t)
+    return TreeBatch(name=cfg["name"], B=B, N=N, V=V, dtype=dt, num_nodes=num_nodes,
+                     parent=torch.as_tensor(parent.astype(np.int32), device=device),
+                     tokens=torch.as_tensor(tokens.astype(np.int32), device=device),
+                     target=target)
+
+
+def tree_from_arrays(target, parent, tokens, num_nodes, dtype="f32", name="custom_tree",
+                     device="cpu") -> TreeBatch:
+    num_nodes = np.asarray(num_nodes, dtype=np.int32)
+    tgt = torch.as_tensor(np.asarray(target, dtype=np.float32)).to(TORCH_DTYPE[dtype])
+    return TreeBatch(name=name, B=int(num_nodes.shape[0]), N=int(num_nodes.sum()),
+                     V=int(tgt.shape[1]), dtype=dtype, num_nodes=num_nodes,
+                     parent=torch.as_tensor(np.asarray(parent, np.int64).astype(np.int32)),
+                     tokens=torch.as_tensor(np.asarray(tokens, np.int64).astype(np.int32)),
+                     target=tgt).to(device)
+
+
+def select_trees(batch: TreeBatch, reqs: Sequence[int], device="cpu") -> TreeBatch:
+    off = batch.offsets
+    rows = []
+    for b in reqs:
+        rows.extend(range(int(off[b]), int(off[b]) + int(batch.num_nodes[b])))
+    ri = torch.as_tensor(rows, dtype=torch.int64, device=batch.target.device)
+    nn = batch.num_nodes[list(reqs)].copy()
+    return TreeBatch(name=batch.name + "_subset", B=len(reqs), N=int(nn.sum()), V=batch.V,
+                     dtype=batch.dtype, num_nodes=nn,
+                     parent=batch.parent.index_select(0, ri).to(device),
+                     tokens=batch.tokens.index_select(0, ri).to(device),
+                     target=batch.target.index_select(0, ri).to(device))
+
+
+def tree_as_numpy(batch: TreeBatch) -> dict:
+    return dict(target=batch.target.detach().to("cpu", torch.float32).numpy(),
+                parent=batch.parent.cpu().numpy().astype(np.int64),
+                tokens=batch.tokens.cpu().numpy().astype(np.int64),
+                num_nodes=batch.num_nodes.astype(np.int64))
