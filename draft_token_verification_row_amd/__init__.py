@@ -26,7 +26,8 @@ _DTYPES = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}
 EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
             "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_early_exit",
             "spec_verify_sample_early_exit", "spec_verify_accept_stats",
-            "spec_verify_set_profile_events")
+            "spec_verify_set_profile_events", "spec_verify_tree_workspace_bytes",
+            "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit")
 
 
 class SvBatch(ctypes.Structure):
@@ -37,6 +38,16 @@ class SvBatch(ctypes.Structure):
         ("target_ld", ctypes.c_int64), ("draft_ld", ctypes.c_int64),
         ("num_draft", ctypes.c_void_p), ("target", ctypes.c_void_p),
         ("draft", ctypes.c_void_p), ("draft_tokens", ctypes.c_void_p),
+    ]
+
+
+class SvTree(ctypes.Structure):
+    """Mirror of sv_tree_t."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("target_ld", ctypes.c_int64),
+        ("num_nodes", ctypes.c_void_p), ("parent", ctypes.c_void_p),
+        ("tokens", ctypes.c_void_p), ("target", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +74,13 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_sample_early_exit.restype = i32
     lib.spec_verify_accept_stats.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.spec_verify_accept_stats.restype = i32
+    lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.spec_verify_tree_workspace_bytes.restype = sz
+    lib.spec_verify_tree_greedy.argtypes = [ctypes.POINTER(SvTree), vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_tree_greedy.restype = i32
+    lib.spec_verify_tree_greedy_early_exit.argtypes = [ctypes.POINTER(SvTree), i32, vp, vp, vp, vp,
+                                                       sz, vp]
+    lib.spec_verify_tree_greedy_early_exit.restype = i32
     lib.spec_verify_set_profile_events.argtypes = [vp, vp]
     lib.spec_verify_set_profile_events.restype = i32
     return lib
@@ -211,6 +229,65 @@ def spec_verify_accept_stats(accepted_len: torch.Tensor, num_draft: torch.Tensor
     if st != SV_OK:
         raise SpecVerifyError(st)
     return out
+
+
+def spec_verify_tree_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(_lib.spec_verify_tree_workspace_bytes(B, N, V))
+
+
+def make_tree_struct(target: torch.Tensor, parent: torch.Tensor, tokens: torch.Tensor,
+                     num_nodes: torch.Tensor) -> SvTree:
+    tld = _rows(target, "target")
+    for name, t in (("parent", parent), ("tokens", tokens), ("num_nodes", num_nodes)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    N = int(parent.numel())
+    if int(tokens.numel()) != N or int(target.shape[0]) < N:
+        raise ValueError("parent, tokens and target rows must cover the same N nodes")
+    return SvTree(B=int(num_nodes.numel()), N=N, V=int(target.shape[1]),
+                  dtype=_DTYPES[target.dtype], target_ld=tld, num_nodes=_ptr(num_nodes),
+                  parent=_ptr(parent), tokens=_ptr(tokens), target=_ptr(target))
+
+
+def spec_verify_tree_greedy(target: torch.Tensor, parent: torch.Tensor, tokens: torch.Tensor,
+                            num_nodes: torch.Tensor, *, max_depth: Optional[int] = None,
+                            accepted_len=None, path_nodes=None, out_tokens=None, workspace=None,
+                            stream=None):
+    """Greedy token-tree verification; returns (accepted_len [B], path_nodes [N],
+    out_tokens [N]) int32 tensors.  With max_depth given, calls the early-exit
+    entry point (reads only the rows the walks visit)."""
+    tr = make_tree_struct(target, parent, tokens, num_nodes)
+    dev = target.device
+    if accepted_len is None:
+        accepted_len = torch.empty(tr.B, dtype=torch.int32, device=dev)
+    if path_nodes is None:
+        path_nodes = torch.empty(tr.N, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(tr.N, dtype=torch.int32, device=dev)
+    need = spec_verify_tree_workspace_bytes(tr.B, tr.N, tr.V)
+    if need == 0:
+        raise SpecVerifyError(SV_ERR_INVALID_ARG)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    ptrs = (_ptr(accepted_len), _ptr(path_nodes), _ptr(out_tokens), _ptr(workspace), wsb,
+            _stream_handle(stream))
+    if max_depth is None:
+        st = _lib.spec_verify_tree_greedy(ctypes.byref(tr), *ptrs)
+    else:
+        st = _lib.spec_verify_tree_greedy_early_exit(ctypes.byref(tr), int(max_depth), *ptrs)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return accepted_len, path_nodes, out_tokens
+
+
+def verify_tree_batch(tb, *, max_depth=None, workspace=None, stream=None):
+    """Run a synthetic tree batch (fields as produced by the input generator)."""
+    nn = torch.as_tensor(tb.num_nodes, dtype=torch.int32, device=tb.target.device)
+    acc, path, out = spec_verify_tree_greedy(tb.target, tb.parent, tb.tokens, nn,
+                                             max_depth=max_depth, workspace=workspace,
+                                             stream=stream)
+    return dict(accepted_len=acc, path_nodes=path, out_tokens=out)
 
 
 def verify_batch(batch, *, workspace=None, want_probs=True, stream=None, max_k=None):

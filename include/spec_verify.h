@@ -169,10 +169,68 @@ int32_t spec_verify_sample_early_exit(const sv_batch_t* batch, int32_t max_k,
 int32_t spec_verify_accept_stats(const int32_t* accepted_len, const int32_t* num_draft,
                                  int32_t B, int32_t max_pos, double* out, void* stream);
 
+/* ---------------------------------------------------------------- token trees
+ * Greedy verification of a draft token tree (chzhyang, "Speculative Decoding:
+ * ...", section 5 "DDTree": the target scores every node with ancestor-only
+ * attention; verification starts at the root and follows the child whose token
+ * is the target's choice at the current node; when no child carries it, that
+ * choice is the bonus token; only the walked path is kept).
+ *
+ * Packed layout.  Request b owns n_b = num_nodes[b] >= 1 nodes; with
+ * noff[b] = n_0 + ... + n_{b-1} and N = noff[B], node i of request b is entry
+ * noff[b] + i of parent / tokens and row noff[b] + i of target.  Node 0 is the
+ * root (the last committed token; its token is not verified); every other
+ * node i has a local parent index 0 <= parent < i.  Row i holds the target's
+ * next-token logits after the prefix ending at node i.
+ *
+ * Greedy choice = lowest id attaining the row maximum.  If several children of
+ * a node carry the chosen token, the lowest node index is followed.
+ * Outputs (device, caller-owned):
+ *   accepted_len [B]  a_b = draft nodes accepted (the root not counted)
+ *   path_nodes   [N]  slots noff[b] + t, t = 0..a_b: local index of the t-th
+ *                     node of the walk (t = 0: the root; its KV entries and
+ *                     those of the listed nodes are the ones to keep)
+ *   out_tokens   [N]  slots noff[b] + t, t < a_b: accepted tokens; slot
+ *                     noff[b] + a_b: the bonus token
+ *   every other slot -1.
+ * Device-side input errors: if sum(num_nodes) != N or some num_nodes[b] < 1
+ * every output is -1; a request with a parent outside [0, node) reports
+ * accepted_len -1 and -1 slots.  Token values outside [0, V) are compared like
+ * any id (they never match a choice).  Other conventions as above. */
+typedef struct sv_tree {
+  int32_t B;                  /* number of requests (trees), >= 1                   */
+  int32_t N;                  /* total nodes, sum of num_nodes, >= B                */
+  int32_t V;                  /* vocabulary size, 1 <= V <= 2^30                    */
+  int32_t dtype;              /* sv_dtype_t of the target logits                    */
+  int64_t target_ld;          /* elements between consecutive target rows, >= V     */
+  const int32_t* num_nodes;   /* device [B]: n_b                                    */
+  const int32_t* parent;      /* device [N]: local parent index (root's ignored)    */
+  const int32_t* tokens;      /* device [N]: token of each node (root's ignored)    */
+  const void* target;         /* device [N][target_ld] logits                       */
+} sv_tree_t;
+
+/* Workspace bytes for a tree call with these sizes (0 for invalid sizes). */
+size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V);
+
+/* Reads every node row once, then walks each tree. */
+int32_t spec_verify_tree_greedy(const sv_tree_t* tree, int32_t* accepted_len,
+                                int32_t* path_nodes, int32_t* out_tokens,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same results, reading only the rows of the nodes the walk visits: step t of
+ * every walk is one round (two kernel launches).  max_depth (0..4096) bounds
+ * a_b: the call runs max_depth + 1 rounds and a request whose walk would
+ * accept more than max_depth nodes is an input error (accepted_len -1, -1
+ * slots).  The tree depth is a safe bound. */
+int32_t spec_verify_tree_greedy_early_exit(const sv_tree_t* tree, int32_t max_depth,
+                                           int32_t* accepted_len, int32_t* path_nodes,
+                                           int32_t* out_tokens, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
  * before and ev_end just after the row-statistics kernel (for the early-exit
- * entry points: around all rounds), on the call's stream.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
+ * entry points: around all rounds), on the call's stream; tree calls too.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
 int32_t spec_verify_set_profile_events(void* ev_begin, void* ev_end);
 
 #ifdef __cplusplus

@@ -192,3 +192,68 @@ def test_early_exit_host_validation(sv):
     assert smp(_batch(sv), 4, ua=None) == INV
     assert smp(_batch(sv), 4, wsb=need - 1) == WS
     assert smp(_batch(sv, draft=None), 4) == INV
+
+
+def _tree(sv, **kw):
+    d = dict(B=2, N=9, V=1000, dtype=0, target_ld=1000, num_nodes=FAKE, parent=FAKE, tokens=FAKE,
+             target=FAKE)
+    d.update(kw)
+    return sv.SvTree(**d)
+
+
+def test_tree_host_validation(sv):
+    INV, UNS, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED, sv.SV_ERR_WORKSPACE
+    need = sv.spec_verify_tree_workspace_bytes(2, 9, 1000)
+    assert need > 0
+    assert sv.spec_verify_tree_workspace_bytes(2, 1, 1000) == 0      # N < B
+    assert sv.spec_verify_tree_workspace_bytes(0, 1, 1000) == 0
+    assert sv.spec_verify_tree_workspace_bytes(1, 1, 0) == 0
+    g = sv._lib.spec_verify_tree_greedy
+    e = sv._lib.spec_verify_tree_greedy_early_exit
+
+    def call(tr, wsb=need, acc=FAKE, path=FAKE, out=FAKE, ws=FAKE):
+        return g(ctypes.byref(tr) if tr is not None else None, acc, path, out, ws, wsb, None)
+
+    assert call(None) == INV
+    assert call(_tree(sv, B=0)) == INV
+    assert call(_tree(sv, N=1)) == INV
+    assert call(_tree(sv, V=0)) == INV
+    assert call(_tree(sv, dtype=3)) == UNS
+    assert call(_tree(sv, target_ld=10)) == INV
+    for f in ("num_nodes", "parent", "tokens", "target"):
+        assert call(_tree(sv, **{f: None})) == INV, f
+    assert call(_tree(sv, target=FAKE + 2)) == INV
+    assert call(_tree(sv), acc=None) == INV
+    assert call(_tree(sv), path=None) == INV
+    assert call(_tree(sv), out=None) == INV
+    assert call(_tree(sv), ws=None) == WS
+    assert call(_tree(sv), wsb=need - 1) == WS
+    for md in (-1, 4097):
+        assert e(ctypes.byref(_tree(sv)), md, FAKE, FAKE, FAKE, FAKE, need, None) == INV
+    assert e(ctypes.byref(_tree(sv)), 3, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WS
+
+
+def test_tree_binding_checks(sv):
+    import torch
+    t = torch.zeros(4, 10)
+    i32 = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sv.make_tree_struct(t, i32.long(), i32, torch.ones(1, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sv.make_tree_struct(t, i32, torch.zeros(3, dtype=torch.int32), torch.ones(1, dtype=torch.int32))
+
+
+def test_tree_synthetic_shapes():
+    import synth
+    tb = synth.make_tree_batch(1)
+    off = tb.offsets
+    par = tb.parent.numpy()
+    tok = tb.tokens.numpy()
+    for b in range(tb.B):
+        s, n = int(off[b]), int(tb.num_nodes[b])
+        assert par[s] == -1
+        for i in range(1, n):
+            assert 0 <= par[s + i] < i
+        for i in range(n):      # sibling tokens are distinct
+            kids = [tok[s + c] for c in range(1, n) if par[s + c] == i]
+            assert len(kids) == len(set(kids))
