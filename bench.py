@@ -12,7 +12,8 @@ k_b per step / step time).  `roofline` describes the row-statistics kernel:
 algorithmic bytes (every logit row it must read, once) over its average
 duration measured with HIP events recorded around it on the call's stream.
 `other_path` times the other entry point (early exit vs all rows) on the same
-batch.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+batch.  `--workload tree` measures greedy token-tree verification instead (32
+trees of 33 nodes over V = 151936 bf16; positions = draft nodes).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload.
 """
 from __future__ import annotations
@@ -32,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (1× MI355X)"
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "tree": "tree"}
 SRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc", "spec_verify.hip")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -98,6 +99,129 @@ def cpu_baseline(batch, min_seconds: float, max_requests: int):
                        f"{t_total:.1f} s of fp64 NumPy on one host core")
 
 
+def cpu_baseline_tree(tb, min_seconds: float):
+    """The tree oracle as it stands, on the first requests, until `min_seconds`."""
+    import synth
+    import oracle
+    done = nodes = 0
+    t_total = 0.0
+    while done < tb.B and t_total < min_seconds:
+        reqs = list(range(done, min(done + 4, tb.B)))
+        sub = synth.select_trees(tb, reqs, device="cpu")
+        d = synth.tree_as_numpy(sub)
+        t0 = time.perf_counter()
+        oracle.tree_verify_batch(**d)
+        t_total += time.perf_counter() - t0
+        nodes += int(sub.num_nodes.sum()) - sub.B
+        done += len(reqs)
+    return dict(value=nodes / t_total if t_total > 0 else None, unit="verified draft positions/s",
+                cores=1, kind="oracle",
+                sample=f"first {done} of {tb.B} trees ({nodes} draft nodes), {t_total:.1f} s of "
+                       f"NumPy on one host core")
+
+
+def bench_tree(args, sv, torch):
+    """Greedy token-tree verification on the tree workload (32 trees of 33 nodes,
+    V = 151936 bf16): headline = all node rows read once, other_path = early exit."""
+    import synth
+    dev = torch.device("cuda:0")
+    tb = synth.make_tree_batch(2, dev)
+    nn = torch.as_tensor(tb.num_nodes, dtype=torch.int32, device=dev)
+    acc = torch.empty(tb.B, dtype=torch.int32, device=dev)
+    path = torch.empty(tb.N, dtype=torch.int32, device=dev)
+    out = torch.empty(tb.N, dtype=torch.int32, device=dev)
+    wsb = sv.spec_verify_tree_workspace_bytes(tb.B, tb.N, tb.V)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    tr = sv.make_tree_struct(tb.target, tb.parent, tb.tokens, nn)
+    sh = torch.cuda.current_stream().cuda_stream
+    par = tb.parent.cpu().numpy()
+    off = tb.offsets
+    depth = 0
+    for b in range(tb.B):
+        d = [0] * int(tb.num_nodes[b])
+        for i in range(1, len(d)):
+            d[i] = d[par[int(off[b]) + i]] + 1
+        depth = max(depth, max(d))
+    lib = sv._lib
+    ptrs = (acc.data_ptr(), path.data_ptr(), out.data_ptr(), ws.data_ptr(), wsb, sh)
+    calls = {False: lambda: lib.spec_verify_tree_greedy(ctypes.byref(tr), *ptrs),
+             True: lambda: lib.spec_verify_tree_greedy_early_exit(ctypes.byref(tr), depth, *ptrs)}
+    ee = args.early_exit
+    for _ in range(args.warmup):
+        assert calls[ee]() == 0
+    torch.cuda.synchronize()
+    if args.profile_only:
+        for _ in range(args.steps):
+            assert calls[ee]() == 0
+        torch.cuda.synchronize()
+        print(f"profile-only: {args.warmup + args.steps} calls of {tb.name}", flush=True)
+        return
+    hip = HipEvents()
+
+    def timed(fn, steps):
+        ev_b, ev_e = hip.create(steps), hip.create(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sv.spec_verify_set_profile_events(None, None)
+        ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
+        hip.destroy(ev_b + ev_e)
+        return (t1 - t0) / steps, float(np.mean(ms)) / 1e3
+
+    es = 4 if tb.dtype == "f32" else 2
+
+    def rows_read(early_exit):
+        if not early_exit:
+            return tb.N
+        return int((acc.cpu().numpy().astype(np.int64) + 1).sum())
+
+    step_s, t_k = timed(calls[ee], args.steps)
+    bytes_k = rows_read(ee) * tb.V * es
+    for _ in range(max(args.warmup // 2, 2)):
+        assert calls[not ee]() == 0
+    o_step, o_t = timed(calls[not ee], max(args.steps // 2, 5))
+    o_bytes = rows_read(not ee) * tb.V * es
+    calls[ee]()
+    torch.cuda.synchronize()
+    positions = tb.N - tb.B
+    achieved = bytes_k / t_k / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC):
+        with open(TRAFFIC) as f:
+            entry = json.load(f).get(tb.name + ("/early_exit" if ee else ""))
+        if entry and entry.get("source_hash") == kernel_source_hash():
+            traffic = entry.get("hbm_bytes_per_launch")
+    path_name = lambda e: f"early exit (max_depth = {depth})" if e else "all node rows"
+    a_np = acc.cpu().numpy()
+    res = {
+        "metric": METRIC, "value": positions / step_s, "unit": "verified draft positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": tb.name, "B": tb.B, "N": tb.N, "V": tb.V, "logits": tb.dtype,
+                   "requests": "greedy token trees", "parallelism": "single GPU",
+                   "path": path_name(ee)},
+        "hbm_gbs_step": bytes_k / step_s / 1e9,
+        "roofline": {"kernel": ("rounds: k_tree_round + k_tree_step_round per step" if ee
+                                else "k_stats (argmax units of every node row)"),
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_k, "avg_kernel_ms": t_k * 1e3},
+        "other_path": {"path": path_name(not ee), "value": positions / o_step,
+                       "ms_per_step": o_step * 1e3, "logit_bytes_read": o_bytes,
+                       "hbm_gbs_step": o_bytes / o_step / 1e9, "timed_interval_ms": o_t * 1e3,
+                       "speedup_of_headline": o_step / step_s},
+        "acceptance": {"mean_accepted_nodes": float(a_np.mean()), "max_accepted": int(a_np.max())},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_tree(tb, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(mib: int, steps: int):
     """A plain copy kernel of known size: reads and writes mib MiB per launch."""
     import torch
@@ -143,6 +267,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "tree":
+        return bench_tree(args, sv, torch)
     cfg_id = WORKLOADS[args.workload]
     batch = synth.make_batch(cfg_id, dev)
     torch.cuda.synchronize()

@@ -66,6 +66,7 @@ constexpr int kUnroll = SV_UNROLL;       // 16-byte loads in flight per lane per
 constexpr int kSegBytes = SV_SEG_BYTES;  // one unit = 32 KiB of one logit row
 constexpr int kSegMinElems = kSegBytes / 4;
 constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
+constexpr int kTreeSegBytes = 4096; // early-exit tree rounds: 4 KiB units (few rows per round)
 constexpr int kRSegMinElems = kRSegBytes / 4;
 constexpr int kBlocksPerCU = 8;      // 32 wavefronts per CU
 constexpr int kPlanThreads = 1024;
@@ -1413,15 +1414,38 @@ __device__ bool tree_parents_ok(const Args& a, const ReqInfo& R, int lane) {
   return !__any(bad);
 }
 
-// One step of the walk for request b at its current node (global row trow):
-// the target's choice from the row's unit partials, then the lowest-index child
+// Lexicographic (max, lowest id) over the unit partials P[0 .. nseg) of one
+// row: lanes over units, then a wavefront reduction (exact in any order).
+__device__ int wave_row_argmax(const Partial* P, int nseg, int lane) {
+  float bm = -INFINITY;
+  int bi = INT_MAX;
+  for (int s = lane; s < nseg; s += kWave) {
+    const Partial p = P[s];
+    if (p.m > bm || (p.m == bm && p.idx < bi)) {
+      bm = p.m;
+      bi = p.idx;
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(bm, o);
+    const int oi = __shfl_xor(bi, o);
+    if (ob > bm || (ob == bm && oi < bi)) {
+      bm = ob;
+      bi = oi;
+    }
+  }
+  return bi;
+}
+
+// One step of the walk for request b at its current node (global row trow),
+// whose unit partials are P: the target's choice, then the lowest-index child
 // of the node carrying that token.  Lane 0 writes the path and token slots.
 // Returns the child's local index, or -1 when the walk ends (acc_len written).
-__device__ int tree_step(const Args& a, int b, const ReqInfo& R, int t, int lane) {
+__device__ int tree_step(const Args& a, int b, const ReqInfo& R, const Partial* P, int t,
+                         int lane) {
   const int cur = R.trow - R.off;
-  int choice = INT_MAX;
-  if (lane == 0) row_argmax(a.ws.pt + (int64_t)R.trow * a.nseg, a.nseg, choice);
-  choice = __shfl(choice, 0);
+  const int choice = wave_row_argmax(P, a.nseg, lane);
   int follow = -1;
   if (choice != INT_MAX) {
     for (int i0 = cur + 1; i0 < R.k && follow < 0; i0 += kWave) {
@@ -1450,7 +1474,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(Args a) {
     ReqInfo R = a.ws.req[b];
     if (!tree_parents_ok(a, R, lane)) continue;   // outputs keep -1
     for (int t = 0;; ++t) {             // every step moves to a higher node index
-      const int f = tree_step(a, b, R, t, lane);
+      const int f = tree_step(a, b, R, a.ws.pt + (int64_t)R.trow * a.nseg, t, lane);
       if (f < 0) break;
       R.trow = R.off + f;
     }
@@ -1458,8 +1482,10 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(Args a) {
 }
 
 // Early-exit rounds: round j streams the row of the current node of every
-// request still walking (argmax units), then one wavefront per such request
-// takes one step.  Lists of walking requests rotate over three buffers.
+// request still walking (argmax units of kTreeSegBytes, partials kept per
+// request: a round reads at most B rows, so small units keep every CU busy),
+// then one wavefront per such request takes one step.  Lists of walking
+// requests rotate over three buffers.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_tree_round(Args a) {
   using Elem = typename L::Elem;
@@ -1476,11 +1502,12 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(Args a) {
   for (int u = gw; u < n_units; u += W) {
     const int w = u / a.nseg;
     const int seg = u - w * a.nseg;
-    const int row = a.ws.req[alive[w]].trow;
+    const int b = alive[w];
+    const int row = a.ws.req[b].trow;
     const int s0 = seg * a.seg;
     const int s1 = min(s0 + a.seg, a.V);
     argmax_unit<L>(tgt + (int64_t)row * a.tld, s0, s1, lane,
-                   a.ws.pt + (int64_t)row * a.nseg + seg);
+                   a.ws.pt + (int64_t)b * a.nseg + seg);
   }
 }
 
@@ -1496,7 +1523,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_step_round(Args a) {
     const int b = a.ws.alive[(int64_t)cur * a.B + w];
     ReqInfo R = a.ws.req[b];
     if (j == 0 && !tree_parents_ok(a, R, lane)) continue;   // outputs keep -1
-    const int f = tree_step(a, b, R, j, lane);
+    const int f = tree_step(a, b, R, a.ws.pt + (int64_t)b * a.nseg, j, lane);
     if (f < 0) continue;
     if (j == a.max_k) {
       // the walk would accept more than max_depth nodes: an input error, the
@@ -1794,12 +1821,14 @@ bool compute_tree_sizes(long long B, long long N, long long V, TreeSizes* z) {
   if (B < 1 || N < B || V < 1 || V > (1ll << 30)) return false;
   if (N >= (1ll << 29)) return false;
   const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
-  if (N * nseg >= (1ll << 31)) return false;
+  const long long ntseg = (V + kTreeSegBytes / 4 - 1) / (kTreeSegBytes / 4);
+  if (N * nseg >= (1ll << 31) || B * ntseg >= (1ll << 31)) return false;
+  const long long npart = std::max(N * nseg, B * ntseg);   // all rows, or per-request rounds
   size_t o = 0;
   z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
   z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);
   z->off_rowdesc = o; o = align_up(o + 4 * (size_t)N, 256);
-  z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)(N * nseg), 256);
+  z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)npart, 256);
   z->off_alive = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
   z->total = o + 256;
   return true;
@@ -1856,7 +1885,7 @@ int32_t run_tree(const sv_tree_t* tr, int32_t* acc_len, int32_t* path, int32_t* 
   a.B = (int)B;
   a.K = (int)N;
   a.V = (int)V;
-  a.seg = kSegBytes / es;
+  a.seg = (early_exit ? kTreeSegBytes : kSegBytes) / es;
   a.nseg = (int)((V + a.seg - 1) / a.seg);
   a.rseg = kRSegBytes / es;
   a.nrseg = (int)((V + a.rseg - 1) / a.rseg);
