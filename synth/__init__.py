@@ -443,3 +443,48 @@ def tree_as_numpy(batch: TreeBatch) -> dict:
                 parent=batch.parent.cpu().numpy().astype(np.int64),
                 tokens=batch.tokens.cpu().numpy().astype(np.int64),
                 num_nodes=batch.num_nodes.astype(np.int64))
+
+
+# ---------------------------------------------------------------------------
+# Confidence-driven verification length.  A drafter proposes a block of N
+# tokens per request with per-position confidences (chzhyang, "Speculative
+# Decoding: ...", section 5 DSpark; blocks of 7 as in the DSpark checkpoints the
+# vLLM blog's tuning section names).  Confidences fall with the position:
+# c_i = clip(c_0 * decay^i + noise, 0, 1), c_0 ~ U(0.6, 1).  The cost table is
+# a synthetic linear one, cost(k) = 1 + slope * k (time units of one round with
+# k verification positions), standing in for the per-deployment profiled table
+# the pages call for.
+
+@dataclasses.dataclass
+class AdaptiveBatch:
+    name: str
+    B: int
+    N: int
+    V: int
+    dtype: str
+    conf: torch.Tensor             # fp32 [B, N]
+    tokens: torch.Tensor           # int32 [B, N]
+    cost: torch.Tensor             # fp64 [N + 1]
+    draft: Optional[torch.Tensor]  # [B * N, V] draft logits (row b * N + i), or None
+
+
+def make_adaptive_batch(B: int = 512, N: int = 7, V: int = 262144, dtype: str = "bf16",
+                        device="cpu", *, slope: float = 0.12, with_rows: bool = True,
+                        seed: Optional[int] = None) -> AdaptiveBatch:
+    ss = np.random.SeedSequence(BASE_SEED + 200 if seed is None else seed)
+    s_conf, s_tok, s_rows = ss.spawn(3)
+    rng = np.random.default_rng(s_conf)
+    c0 = rng.uniform(0.6, 1.0, size=(B, 1))
+    decay = rng.uniform(0.75, 0.97, size=(B, 1))
+    conf = np.clip(c0 * decay ** np.arange(N)[None, :] + rng.normal(0, 0.05, size=(B, N)), 0, 1)
+    tokens = np.random.default_rng(s_tok).integers(0, V, size=(B, N))
+    cost = 1.0 + slope * np.arange(N + 1, dtype=np.float64)
+    draft = None
+    if with_rows:
+        g = _torch_gen(s_rows, device)
+        draft = (torch.randn((B * N, V), generator=g, device=device, dtype=torch.float32)
+                 * 2.0).to(TORCH_DTYPE[dtype])
+    return AdaptiveBatch(name=f"adaptive_block{N}_v{V}", B=B, N=N, V=V, dtype=dtype,
+                         conf=torch.as_tensor(conf.astype(np.float32), device=device),
+                         tokens=torch.as_tensor(tokens.astype(np.int32), device=device),
+                         cost=torch.as_tensor(cost, device=device), draft=draft)
