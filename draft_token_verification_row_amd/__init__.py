@@ -27,7 +27,8 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
             "spec_verify_greedy", "spec_verify_sample", "spec_verify_greedy_early_exit",
             "spec_verify_sample_early_exit", "spec_verify_accept_stats",
             "spec_verify_set_profile_events", "spec_verify_tree_workspace_bytes",
-            "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit")
+            "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit",
+            "spec_verify_adaptive_length", "spec_verify_gather_rows")
 
 
 class SvBatch(ctypes.Structure):
@@ -81,6 +82,11 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_tree_greedy_early_exit.argtypes = [ctypes.POINTER(SvTree), i32, vp, vp, vp, vp,
                                                        sz, vp]
     lib.spec_verify_tree_greedy_early_exit.restype = i32
+    lib.spec_verify_adaptive_length.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_verify_adaptive_length.restype = i32
+    lib.spec_verify_gather_rows.argtypes = [i32, i32, vp, ctypes.c_int64, i32, vp, vp, i32, vp,
+                                            ctypes.c_int64, vp]
+    lib.spec_verify_gather_rows.restype = i32
     lib.spec_verify_set_profile_events.argtypes = [vp, vp]
     lib.spec_verify_set_profile_events.restype = i32
     return lib
@@ -288,6 +294,48 @@ def verify_tree_batch(tb, *, max_depth=None, workspace=None, stream=None):
                                              max_depth=max_depth, workspace=workspace,
                                              stream=stream)
     return dict(accepted_len=acc, path_nodes=path, out_tokens=out)
+
+
+def spec_verify_adaptive_length(conf: torch.Tensor, cost: torch.Tensor, draft_tokens: torch.Tensor,
+                                *, want_src_index: bool = True, want_progress: bool = True,
+                                stream=None) -> dict:
+    """Per-request verification length from confidences [B, N] (fp32) and a cost
+    table [N + 1] (fp64); returns device tensors num_draft [B], offsets [B + 1],
+    tokens [B * N] (first offsets[B] entries used), src_index [B * N], progress [B]."""
+    if conf.dim() != 2 or conf.dtype != torch.float32 or not conf.is_contiguous():
+        raise ValueError("conf must be a contiguous float32 [B, N] tensor")
+    B, N = conf.shape
+    if cost.dtype != torch.float64 or cost.numel() != N + 1:
+        raise ValueError("cost must be a float64 tensor of N + 1 entries")
+    if draft_tokens.dtype != torch.int32 or draft_tokens.numel() != B * N \
+            or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be a contiguous int32 [B, N] tensor")
+    dev = conf.device
+    nd = torch.empty(B, dtype=torch.int32, device=dev)
+    off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    toks = torch.empty(max(B * N, 1), dtype=torch.int32, device=dev)
+    src = torch.empty(max(B * N, 1), dtype=torch.int32, device=dev) if want_src_index else None
+    prog = torch.empty(B, dtype=torch.float64, device=dev) if want_progress else None
+    st = _lib.spec_verify_adaptive_length(B, N, _ptr(conf), _ptr(cost), _ptr(draft_tokens),
+                                          _ptr(nd), _ptr(off), _ptr(toks), _ptr(src), _ptr(prog),
+                                          _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return dict(num_draft=nd, offsets=off, tokens=toks, src_index=src, progress=prog)
+
+
+def spec_verify_gather_rows(src: torch.Tensor, index: torch.Tensor, count: torch.Tensor,
+                            max_rows: int, *, out=None, stream=None) -> torch.Tensor:
+    """dst[r] = src[index[r]] for r < min(count[0], max_rows) (count on the device)."""
+    ld = _rows(src, "src")
+    if out is None:
+        out = torch.empty(max(max_rows, 1), src.shape[1], dtype=src.dtype, device=src.device)
+    st = _lib.spec_verify_gather_rows(_DTYPES[src.dtype], int(src.shape[1]), _ptr(src), ld,
+                                      int(src.shape[0]), _ptr(index), _ptr(count), int(max_rows),
+                                      _ptr(out), _rows(out, "out"), _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return out
 
 
 def verify_batch(batch, *, workspace=None, want_probs=True, stream=None, max_k=None):

@@ -227,10 +227,53 @@ int32_t spec_verify_tree_greedy_early_exit(const sv_tree_t* tree, int32_t max_de
                                            int32_t* out_tokens, void* workspace,
                                            size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- adaptive length
+ * Confidence-driven verification length and compaction (chzhyang, "Speculative
+ * Decoding: ...", section 5 DSpark: s_j = c_1 ... c_j estimates the chance of
+ * accepting through position j and a window of k positions has estimated
+ * progress 1 + s_1 + ... + s_k; section 2: the time per committed token is the
+ * round's cost over its progress; section 9: the cost of each window length
+ * comes from a table profiled for the deployment).
+ *
+ * Request b has a drafted block of N tokens (draft_tokens[b*N + i]) with
+ * confidences conf[b*N + i] (fp32, used as given).  It keeps its first k_b
+ * tokens, k_b in 0..N maximising (1 + s_1 + ... + s_k) / cost[k]; ties go to
+ * the smallest k.  Arithmetic is fp64 in the order s = s * c_j,
+ * total = total + s, ratio = total / cost[k] (correctly rounded), so the choice
+ * is reproducible bit for bit.  Outputs (device, caller-owned):
+ *   num_draft  [B]    k_b (the num_draft of the packed batch to verify)
+ *   offsets    [B+1]  exclusive prefix sums of k_b; offsets[B] = K'
+ *   tokens_out [B*N]  capacity; the first K' entries are the kept tokens,
+ *                     request after request
+ *   src_index  [B*N]  or NULL: b*N + i for each kept token (its row in the
+ *                     drafter's [B*N] row layout, e.g. for
+ *                     spec_verify_gather_rows)
+ *   progress   [B]    or NULL: 1 + s_1 + ... + s_{k_b}
+ * A cost table entry that is not a positive finite number is a device-side
+ * input error: every num_draft and progress is -1, every offset 0, nothing is
+ * compacted.  1 <= B, 0 <= N <= 4096.  One workgroup. */
+int32_t spec_verify_adaptive_length(int32_t B, int32_t N, const float* conf,
+                                    const double* cost, const int32_t* draft_tokens,
+                                    int32_t* num_draft, int32_t* offsets,
+                                    int32_t* tokens_out, int32_t* src_index,
+                                    double* progress, void* stream);
+
+/* Row gather for the compacted batch: dst row r = src row index[r] for
+ * r < min(*count, max_rows) (count is a device pointer, e.g. &offsets[B] of
+ * spec_verify_adaptive_length, so no host synchronisation is needed).  Rows
+ * hold V elements of dtype; src_ld, dst_ld >= V are row strides in elements;
+ * index has at least max_rows entries; a row whose index lies outside
+ * [0, src_rows) is left unwritten.  An HBM-bound copy (nontemporal 16-byte
+ * loads and stores when pointers and strides are 16-byte aligned). */
+int32_t spec_verify_gather_rows(int32_t dtype, int32_t V, const void* src, int64_t src_ld,
+                                int32_t src_rows, const int32_t* index, const int32_t* count,
+                                int32_t max_rows, void* dst, int64_t dst_ld, void* stream);
+
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
  * before and ev_end just after the row-statistics kernel (for the early-exit
- * entry points: around all rounds), on the call's stream; tree calls too.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
+ * entry points: around all rounds), on the call's stream; tree calls too, and
+ * spec_verify_gather_rows around its copy kernel.  Pass NULL, NULL to stop.  Thread-local; returns SV_OK. */
 int32_t spec_verify_set_profile_events(void* ev_begin, void* ev_end);
 
 #ifdef __cplusplus

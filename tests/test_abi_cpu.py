@@ -257,3 +257,28 @@ def test_tree_synthetic_shapes():
         for i in range(n):      # sibling tokens are distinct
             kids = [tok[s + c] for c in range(1, n) if par[s + c] == i]
             assert len(kids) == len(set(kids))
+
+
+def test_adaptive_and_gather_host_validation(sv):
+    INV, UNS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED
+    f = sv._lib.spec_verify_adaptive_length
+    assert f(0, 7, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 4097, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 7, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 7, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 7, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 7, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == INV
+    assert f(4, 7, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == INV
+    assert f(4, 7, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == INV
+    g = sv._lib.spec_verify_gather_rows
+    assert g(5, 100, FAKE, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == UNS
+    assert g(1, 0, FAKE, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 99, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 100, 4, FAKE, FAKE, 4, FAKE, 50, None) == INV
+    assert g(1, 100, None, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 100, 4, None, FAKE, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 100, 4, FAKE, None, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 100, 4, FAKE, FAKE, -1, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE + 1, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
+    assert g(1, 100, FAKE, 100, 4, FAKE, FAKE, 0, FAKE, 100, None) == sv.SV_OK   # nothing to copy
