@@ -13,7 +13,9 @@ algorithmic bytes (every logit row it must read, once) over its average
 duration measured with HIP events recorded around it on the call's stream.
 `other_path` times the other entry point (early exit vs all rows) on the same
 batch.  `--workload tree` measures greedy token-tree verification instead (32
-trees of 33 nodes over V = 151936 bf16; positions = draft nodes).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+trees of 33 nodes over V = 151936 bf16; positions = draft nodes), and
+`--workload adaptive` the confidence-driven length choice plus the gather of
+the kept draft rows (512 blocks of 7 over V = 262144 bf16).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload.
 """
 from __future__ import annotations
@@ -33,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (1× MI355X)"
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "tree": "tree"}
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "tree": "tree", "adaptive": "adaptive"}
 SRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc", "spec_verify.hip")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -222,6 +224,91 @@ def bench_tree(args, sv, torch):
     print(json.dumps(res), flush=True)
 
 
+def bench_adaptive(args, sv, torch):
+    """Confidence-driven verification length for 512 requests with blocks of 7
+    drafts over V = 262144 bf16 draft rows: one step = choose every k_b, pack the
+    kept tokens, gather the kept draft rows into the packed layout."""
+    import synth
+    import oracle
+    dev = torch.device("cuda:0")
+    ab = synth.make_adaptive_batch(B=512, N=7, V=262144, dtype="bf16", device=dev)
+    B, N, V = ab.B, ab.N, ab.V
+    lib = sv._lib
+    nd = torch.empty(B, dtype=torch.int32, device=dev)
+    off = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    toks = torch.empty(B * N, dtype=torch.int32, device=dev)
+    src = torch.empty(B * N, dtype=torch.int32, device=dev)
+    prog = torch.empty(B, dtype=torch.float64, device=dev)
+    out = torch.empty(B * N, V, dtype=ab.draft.dtype, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    cnt = off[B:]
+
+    def step():
+        assert lib.spec_verify_adaptive_length(B, N, ab.conf.data_ptr(), ab.cost.data_ptr(),
+                                               ab.tokens.data_ptr(), nd.data_ptr(), off.data_ptr(),
+                                               toks.data_ptr(), src.data_ptr(), prog.data_ptr(), sh) == 0
+        assert lib.spec_verify_gather_rows(1, V, ab.draft.data_ptr(), V, B * N, src.data_ptr(),
+                                           cnt.data_ptr(), B * N, out.data_ptr(), V, sh) == 0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.profile_only:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        print(f"profile-only: {args.warmup + args.steps} steps of {ab.name}", flush=True)
+        return
+    hip = HipEvents()
+    ev_b, ev_e = hip.create(args.steps), hip.create(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sv.spec_verify_set_profile_events(None, None)
+    g_ms = float(np.mean([hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(args.steps)]))
+    hip.destroy(ev_b + ev_e)
+    step_s = (t1 - t0) / args.steps
+    K = int(off[B].item())
+    bytes_g = 2 * K * V * 2                   # each kept row read once and written once
+    achieved = bytes_g / (g_ms / 1e3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC):
+        with open(TRAFFIC) as f:
+            entry = json.load(f).get(ab.name)
+        if entry and entry.get("source_hash") == kernel_source_hash():
+            traffic = entry.get("hbm_bytes_per_launch")
+    res = {
+        "metric": METRIC, "value": K / step_s, "unit": "draft positions scheduled for verification/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": step_s * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": ab.name, "B": B, "N": N, "V": V, "logits": ab.dtype,
+                   "cost_table": ab.cost.cpu().numpy().tolist(), "kept_positions": K,
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_gather_rows (kept draft rows into the packed layout)", "bound": "hbm",
+                     "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_g, "avg_kernel_ms": g_ms},
+        "mean_progress": float(prog.mean().item()),
+    }
+    if not args.no_cpu_baseline:
+        c, co, tk = ab.conf.cpu().numpy(), ab.cost.cpu().numpy(), ab.tokens.cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 2 or reps == 0:
+            oracle.adaptive_batch(c, co, tk)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": K / dt, "unit": res["unit"], "cores": 1, "kind": "oracle",
+                               "sample": f"the whole selection and packing ({B} requests) x {reps}, "
+                                         "no row gather (the oracle packs indices only)"}
+    print(json.dumps(res), flush=True)
+
+
 def copy_probe(mib: int, steps: int):
     """A plain copy kernel of known size: reads and writes mib MiB per launch."""
     import torch
@@ -269,6 +356,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "tree":
         return bench_tree(args, sv, torch)
+    if args.workload == "adaptive":
+        return bench_adaptive(args, sv, torch)
     cfg_id = WORKLOADS[args.workload]
     batch = synth.make_batch(cfg_id, dev)
     torch.cuda.synchronize()
