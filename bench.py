@@ -507,11 +507,20 @@ def main():
             "speedup_of_headline": o_step / step_s,
         },
     }
-    st = sv.spec_verify_accept_stats(acc, nd, max(kmax, 1)).cpu().numpy()
+    st_out = torch.empty(4 + max(kmax, 1), dtype=torch.float64, device=dev)
+    sv.spec_verify_accept_stats(acc, nd, max(kmax, 1), out=st_out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(50):
+        sv.spec_verify_accept_stats(acc, nd, max(kmax, 1), out=st_out)
+    e1.record()
+    torch.cuda.synchronize()
+    st = st_out.cpu().numpy()
     res["acceptance"] = {
         "note": "from the timed calls' outputs; MAL counts the correction/bonus token, AR = kept/proposed drafts",
         "mean_kept_drafts": float(st[1]), "MAL": float(st[2]), "AR": float(st[3]),
         "per_position": [round(float(x), 4) for x in st[4:4 + max(kmax, 1)]],
+        "stats_call_us": e0.elapsed_time(e1) * 1e3 / 50,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, max_requests=batch.B)
