@@ -63,6 +63,16 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 #define SV_SEG_BYTES 32768
 #endif
 constexpr int kUnroll = SV_UNROLL;       // 16-byte loads in flight per lane per row
+#ifndef SV_ROUND_UNROLL
+#define SV_ROUND_UNROLL 4
+#endif
+// early-exit rounds: same per-lane chunk order (so the same partials bit for
+// bit), more loads in flight for the small late rounds
+constexpr int kRoundUnroll = SV_ROUND_UNROLL;
+#ifndef SV_RESID_UNROLL
+#define SV_RESID_UNROLL 4
+#endif
+constexpr int kResidUnroll = SV_RESID_UNROLL;   // k_resid: loads in flight per lane per row
 constexpr int kSegBytes = SV_SEG_BYTES;  // one unit = 32 KiB of one logit row
 constexpr int kSegMinElems = kSegBytes / 4;
 constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
@@ -224,22 +234,22 @@ __device__ __forceinline__ double wave_sum(double x) {
 
 // Visit the unit [s0, s1) of one row, chunk by chunk, in increasing id order
 // per lane.  f(v, first_id, count) receives E values (padding = -inf).
-template <class L, class F>
+template <class L, int U, class F>
 __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, int s1,
                                          int lane, F& f) {
   constexpr int E = L::E;
   const int n = s1 - s0;
   const int nchunk = n / E;
   const typename L::Elem* p = row + s0;
-  constexpr int per_it = kWave * kUnroll;
+  constexpr int per_it = kWave * U;
   const int nit = nchunk / per_it;
   int c = lane;
   for (int it = 0; it < nit; ++it, c += per_it) {
-    typename L::Raw r[kUnroll];
+    typename L::Raw r[U];
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
+    for (int j = 0; j < U; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
 #pragma unroll
-    for (int j = 0; j < kUnroll; ++j) {
+    for (int j = 0; j < U; ++j) {
       float v[E];
       L::unpack(r[j], v);
       f(v, s0 + (c + j * kWave) * E, E);
@@ -301,7 +311,7 @@ struct ArgmaxAcc {
   }
 };
 
-template <class L>
+template <class L, int U = kUnroll>
 __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
                              const Args& a, Partial* out) {
   SoftmaxAcc<L::E> acc;
@@ -310,7 +320,7 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
   acc.c_lo = a.c_lo;
 #pragma unroll
   for (int e = 0; e < L::E; ++e) acc.s[e] = 0.f;
-  for_unit<L>(row, s0, s1, lane, acc);
+  for_unit<L, U>(row, s0, s1, lane, acc);
   float sl = 0.f;
 #pragma unroll
   for (int e = 0; e < L::E; ++e) sl += acc.s[e];
@@ -326,13 +336,13 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
   }
 }
 
-template <class L>
+template <class L, int U = kUnroll>
 __device__ void argmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
                             Partial* out) {
   ArgmaxAcc<L::E> acc;
   acc.best = -INFINITY;
   acc.idx = INT_MAX;
-  for_unit<L>(row, s0, s1, lane, acc);
+  for_unit<L, U>(row, s0, s1, lane, acc);
   float b = acc.best;
   int i = acc.idx;
 #pragma unroll
@@ -823,7 +833,7 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
     }
     const int s0 = seg * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
-    const double tot = resid_unit<L, 4>(tp, dp, fw, R.y, s0, s1, lane);
+    const double tot = resid_unit<L, kResidUnroll>(tp, dp, fw, R.y, s0, s1, lane);
     if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
   }
 }
@@ -1293,9 +1303,9 @@ __global__ __launch_bounds__(kBlock) void k_round(Args a) {
       const Elem* base = is_draft ? drf + (int64_t)row * a.dld : tgt + (int64_t)row * a.tld;
       Partial* out = (is_draft ? a.ws.pd : a.ws.pt) + (int64_t)row * a.nseg + seg;
       if (desc & kGreedyBit)
-        argmax_unit<L>(base, s0, s1, lane, out);
+        argmax_unit<L, kRoundUnroll>(base, s0, s1, lane, out);
       else
-        softmax_unit<L>(base, s0, s1, lane, a, out);
+        softmax_unit<L, kRoundUnroll>(base, s0, s1, lane, a, out);
     } else {                            // residual unit of a request cut at j - 1
       const int v = u - n_s;
       const int ri = v / a.nrseg;
@@ -1306,7 +1316,7 @@ __global__ __launch_bounds__(kBlock) void k_round(Args a) {
       const Elem* dp = drf + (int64_t)R.drow * a.dld;
       const int s0 = seg * a.rseg;
       const int s1 = min(s0 + a.rseg, a.V);
-      const double tot = resid_unit<L, kUnroll>(tp, dp, resid_weights(R, a), R.y, s0, s1, lane);
+      const double tot = resid_unit<L, kRoundUnroll>(tp, dp, resid_weights(R, a), R.y, s0, s1, lane);
       if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
     }
   }
