@@ -334,6 +334,8 @@ def main():
     ap.add_argument("--early-exit", action="store_true",
                     help="headline = the early-exit entry points (rows read only up to each cut); "
                          "the all-rows path is then reported under other_path, and vice versa")
+    ap.add_argument("--launch-plan", default="auto", choices=["auto", "multi", "single"],
+                    help="launch plan of the all-rows entry points (library default: auto)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -354,6 +356,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    sv.spec_verify_set_launch_plan({"auto": 0, "multi": 1, "single": 2}[args.launch_plan])
     if args.workload == "tree":
         return bench_tree(args, sv, torch)
     if args.workload == "adaptive":
@@ -481,6 +484,7 @@ def main():
                          f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
             "parallelism": "single GPU",
             "path": path(ee),
+            "launch_plan": args.launch_plan,
         },
         "rows_per_s": (batch.K + batch.B) / step_s,
         "hbm_gbs_step": bytes_stats / step_s / 1e9,

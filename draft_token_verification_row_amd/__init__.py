@@ -28,7 +28,8 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
             "spec_verify_sample_early_exit", "spec_verify_accept_stats",
             "spec_verify_set_profile_events", "spec_verify_tree_workspace_bytes",
             "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit",
-            "spec_verify_adaptive_length", "spec_verify_gather_rows")
+            "spec_verify_adaptive_length", "spec_verify_gather_rows",
+            "spec_verify_set_launch_plan")
 
 
 class SvBatch(ctypes.Structure):
@@ -87,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_gather_rows.argtypes = [i32, i32, vp, ctypes.c_int64, i32, vp, vp, i32, vp,
                                             ctypes.c_int64, vp]
     lib.spec_verify_gather_rows.restype = i32
+    lib.spec_verify_set_launch_plan.argtypes = [i32]
+    lib.spec_verify_set_launch_plan.restype = i32
     lib.spec_verify_set_profile_events.argtypes = [vp, vp]
     lib.spec_verify_set_profile_events.restype = i32
     return lib
@@ -125,6 +128,13 @@ def spec_verify_workspace_bytes(B: int, K: int, V: int) -> int:
 
 def spec_verify_status_string(status: int) -> str:
     return _lib.spec_verify_status_string(status).decode()
+
+
+def spec_verify_set_launch_plan(plan: int) -> None:
+    """0 automatic, 1 multi-kernel pipeline, 2 single launch (calling thread only)."""
+    st = _lib.spec_verify_set_launch_plan(int(plan))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
 
 
 def spec_verify_set_profile_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:

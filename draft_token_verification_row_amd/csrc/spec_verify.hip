@@ -568,26 +568,11 @@ __device__ __forceinline__ float logit_at(const void* base, int64_t row, int64_t
 // One wavefront per request.  Positions are taken 32 at a time: lane l < 32
 // combines the target row of position base+l, lane l+32 the draft row of the
 // same position, so every row of a request is combined in parallel.
+// Decision of every position of request b by one wavefront (all rows' partials
+// are in the workspace).  queue: list the request for k_resid when it needs a
+// residual sweep (the single-launch path sweeps it in the same workgroup).
 template <class D>
-__global__ __launch_bounds__(kBlock) void k_decide(Args a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (a.ws.hdr->error) {
-    // inconsistent num_draft: every output slot becomes -1
-    const long long gt = (long long)blockIdx.x * kBlock + threadIdx.x;
-    const long long gs = (long long)gridDim.x * kBlock;
-    for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
-    for (long long i = gt; i < a.B; i += gs) {
-      a.acc_len[i] = -1;
-      if (a.resid_out) a.resid_out[i] = -1.f;
-    }
-    for (long long i = gt; i < a.K; i += gs) {
-      if (a.p_out) a.p_out[i] = -1.f;
-      if (a.q_out) a.q_out[i] = -1.f;
-    }
-    return;
-  }
-  if (b >= a.B) return;
+__device__ void decide_request(const Args& a, int b, int lane, bool queue) {
   const ReqInfo R = a.ws.req[b];
   const int k = R.k;
   const int trow0 = R.off + b;
@@ -698,8 +683,10 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
         W.y = a.tokens[drow0 + A];
         W.Mq = MqA;
         W.Sq = SqA;
-        const int j = atomicAdd(&a.ws.hdr->n_resid, 1);
-        a.ws.resid_list[j] = b;
+        if (queue) {
+          const int j = atomicAdd(&a.ws.hdr->n_resid, 1);
+          a.ws.resid_list[j] = b;
+        }
       } else {
         W.kind = KIND_BONUS;
         W.drow = -1;
@@ -708,6 +695,30 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
     }
     a.ws.req[b] = W;
   }
+}
+
+
+template <class D>
+__global__ __launch_bounds__(kBlock) void k_decide(Args a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (a.ws.hdr->error) {
+    // inconsistent num_draft: every output slot becomes -1
+    const long long gt = (long long)blockIdx.x * kBlock + threadIdx.x;
+    const long long gs = (long long)gridDim.x * kBlock;
+    for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
+    for (long long i = gt; i < a.B; i += gs) {
+      a.acc_len[i] = -1;
+      if (a.resid_out) a.resid_out[i] = -1.f;
+    }
+    for (long long i = gt; i < a.K; i += gs) {
+      if (a.p_out) a.p_out[i] = -1.f;
+      if (a.q_out) a.q_out[i] = -1.f;
+    }
+    return;
+  }
+  if (b >= a.B) return;
+  decide_request<D>(a, b, lane, true);
 }
 
 // ------------------------------------------------------------------ draw weights
@@ -906,9 +917,36 @@ __device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, do
   }
 }
 
-// Rescan one unit of PER*kBlock ids with every weight cached in registers;
-// block-wide exclusive scan of the per-thread sums, then the owning thread walks
-// its ids in ascending order.
+// Weights of the ids [id0, id0 + E) of a unit ending at s1 (0 past s1 and at y).
+template <class L, class WF>
+__device__ __forceinline__ void unit_weights(const typename L::Elem* tp, const typename L::Elem* dp,
+                                             int id0, int s1, int y, const WF& wf, float* w) {
+  constexpr int E = L::E;
+  float vt[E], vd[E];
+  if (id0 + E <= s1) {
+    L::unpack(L::load(tp + id0), vt);
+    if (dp) L::unpack(L::load(dp + id0), vd);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      vt[e] = (id0 + e < s1) ? L::one(tp + id0 + e) : -INFINITY;
+      vd[e] = (dp && id0 + e < s1) ? L::one(dp + id0 + e) : 0.f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float x;
+    if constexpr (std::is_same<WF, ResidW>::value) x = wf(vt[e], vd[e]);
+    else x = wf(vt[e]);
+    w[e] = (id0 + e < s1 && id0 + e != y) ? x : 0.f;
+  }
+}
+
+// Rescan one unit of PER * kBlock ids: thread t (< kBlock) sums the weights of
+// its PER ids in ascending order, a block-wide exclusive scan of those sums
+// locates the crossing thread, which walks its ids again.  In a block larger
+// than kBlock the extra threads take part in the barriers only, so the result
+// is the same for any block size.
 template <class L, int PER, class WF>
 __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* dp, int s0,
                            int s1, int y, const WF& wf, double before, double thr, int fallback,
@@ -918,43 +956,29 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid >> 6;
+  const bool active = tid < kBlock;
   const int v0 = s0 + tid * PER;
-  float w[PER];
+  double ts = 0.0;
+  if (active) {
 #pragma unroll
-  for (int c = 0; c < PER / E; ++c) {
-    const int id0 = v0 + c * E;
-    float vt[E], vd[E];
-    if (id0 + E <= s1) {
-      L::unpack(L::load(tp + id0), vt);
-      if (dp) L::unpack(L::load(dp + id0), vd);
-    } else {
+    for (int c = 0; c < PER / E; ++c) {
+      float w[E];
+      unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        vt[e] = (id0 + e < s1) ? L::one(tp + id0 + e) : -INFINITY;
-        vd[e] = (dp && id0 + e < s1) ? L::one(dp + id0 + e) : 0.f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float x;
-      if constexpr (std::is_same<WF, ResidW>::value) x = wf(vt[e], vd[e]);
-      else x = wf(vt[e]);
-      w[c * E + e] = (id0 + e < s1 && id0 + e != y) ? x : 0.f;
+      for (int e = 0; e < E; ++e) ts += (double)w[e];
     }
   }
-  double ts = 0.0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) ts += (double)w[j];
   const double incl_w = wave_incl_scan(ts, lane);
-  if (lane == kWave - 1) s_wave[wv] = incl_w;
+  if (active && lane == kWave - 1) s_wave[wv] = incl_w;
   if (tid == 0) *s_owner = INT_MAX;
   __syncthreads();
   double wprefix = 0.0;
-  for (int q = 0; q < wv; ++q) wprefix += s_wave[q];
+  if (active)
+    for (int q = 0; q < wv; ++q) wprefix += s_wave[q];
   const double prev = __shfl_up(incl_w, 1);
   const double excl = before + wprefix + (lane == 0 ? 0.0 : prev);
   const double incl = before + wprefix + incl_w;
-  if (!fallback && incl > thr && ts > 0.0) atomicMin(s_owner, tid);
+  if (active && !fallback && incl > thr && ts > 0.0) atomicMin(s_owner, tid);
   __syncthreads();
   int owner = *s_owner;
   if (owner == INT_MAX) {
@@ -962,14 +986,18 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
     __syncthreads();
     if (tid == 0) *s_owner = -1;
     __syncthreads();
-    if (ts > 0.0) atomicMax(s_owner, tid);
+    if (active && ts > 0.0) atomicMax(s_owner, tid);
     __syncthreads();
     owner = *s_owner;
     if (tid == owner) {
       int tok = -1;
+      for (int c = 0; c < PER / E; ++c) {
+        float w[E];
+        unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
 #pragma unroll
-      for (int j = 0; j < PER; ++j)
-        if (w[j] > 0.f) tok = v0 + j;
+        for (int e = 0; e < E; ++e)
+          if (w[e] > 0.f) tok = v0 + c * E + e;
+      }
       return tok;
     }
     return -2;
@@ -977,27 +1005,33 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
   if (tid != owner) return -2;
   double cum = excl;
   int tok = -1, last = -1;
+  for (int c = 0; c < PER / E; ++c) {
+    float w[E];
+    unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    cum += (double)w[j];
-    if (w[j] > 0.f) last = v0 + j;
-    if (tok < 0 && cum > thr) tok = v0 + j;
+    for (int e = 0; e < E; ++e) {
+      cum += (double)w[e];
+      if (w[e] > 0.f) last = v0 + c * E + e;
+      if (tok < 0 && cum > thr) tok = v0 + c * E + e;
+    }
   }
   return tok >= 0 ? tok : last;
 }
 
+struct FinalizeShared {
+  double wave[kWavesPerBlock];
+  double before, thr, Z;
+  int unit, mode, fallback, owner;
+};
+
+// Correction or bonus draw of request b by one block of >= kBlock threads.
 template <class L>
-__global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
+__device__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
   using Elem = typename L::Elem;
   constexpr int PER_S = kSegBytes / (int)sizeof(Elem) / kBlock;    // k_stats unit
   constexpr int PER_R = kRSegBytes / (int)sizeof(Elem) / kBlock;   // k_resid unit
-  __shared__ double s_wave[kWavesPerBlock];
-  __shared__ double s_before, s_thr, s_Z;
-  __shared__ int s_unit, s_mode, s_fallback, s_owner;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int b = blockIdx.x;
-  if (a.ws.hdr->error) return;
   const ReqInfo R = a.ws.req[b];
   if (R.kind != KIND_RESID && R.kind != KIND_BONUS) return;
   const double w = (double)a.u_final[b];
@@ -1020,35 +1054,161 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
       find_unit(um, a.nseg, w, lane, Z, unit, before, fb);
     }
     if (tid == 0) {
-      s_unit = unit;
-      s_before = before;
-      s_thr = w * Z;
-      s_Z = Z;
-      s_mode = mode;
-      s_fallback = fb;
+      sh.unit = unit;
+      sh.before = before;
+      sh.thr = w * Z;
+      sh.Z = Z;
+      sh.mode = mode;
+      sh.fallback = fb;
     }
   }
   __syncthreads();
-  const int mode = s_mode;
+  const int mode = sh.mode;
   const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
   int tok;
   if (mode == DRAW_RESID) {
     const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
-    const int s0 = s_unit * a.rseg;
+    const int s0 = sh.unit * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
-    tok = rescan_unit<L, PER_R>(tp, dp, s0, s1, R.y, resid_weights(R, a), s_before, s_thr,
-                                s_fallback, s_wave, &s_owner);
+    tok = rescan_unit<L, PER_R>(tp, dp, s0, s1, R.y, resid_weights(R, a), sh.before, sh.thr,
+                                sh.fallback, sh.wave, &sh.owner);
   } else {
-    const int s0 = s_unit * a.seg;
+    const int s0 = sh.unit * a.seg;
     const int s1 = min(s0 + a.seg, a.V);
     tok = rescan_unit<L, PER_S>(tp, (const Elem*)nullptr, s0, s1, -1, target_weights(R, a),
-                                s_before, s_thr, s_fallback, s_wave, &s_owner);
+                                sh.before, sh.thr, sh.fallback, sh.wave, &sh.owner);
   }
   if (tok != -2) {
     a.out[R.trow] = tok;
     if (a.resid_out)
-      a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? s_Z : 0.0) : -1.f;
+      a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? sh.Z : 0.0) : -1.f;
   }
+}
+
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
+  __shared__ FinalizeShared sh;
+  if (a.ws.hdr->error) return;
+  finalize_request<L>(a, blockIdx.x, sh);
+}
+
+// ------------------------------------------------------------------ single-launch path
+// Small batches: one workgroup of kFusedThreads threads per request runs the
+// whole step (offsets, row statistics, decisions, residual sweep, draw) with
+// only block barriers between the phases, so a call is one launch instead of
+// five.  Every phase calls the same unit, combine, decide and draw code as the
+// multi-kernel path, so the results are the same bit for bit.
+constexpr int kFusedThreads = 1024;
+constexpr int kFusedWaves = kFusedThreads / kWave;
+constexpr int kFusedUnroll = 8;
+
+template <class L>
+__global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
+  __shared__ FinalizeShared sh;
+  __shared__ long long s_pre[kFusedWaves], s_tot[kFusedWaves];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
+  const int b = blockIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  // offsets: every workgroup sums num_draft itself (B is small on this path)
+  long long pre = 0, tot = 0;
+  for (int i = tid; i < a.B; i += kFusedThreads) {
+    const int k = a.num_draft[i];
+    if (k < 0 || k > a.K) s_bad = 1;
+    else {
+      tot += k;
+      if (i < b) pre += k;
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    pre += __shfl_xor(pre, o);
+    tot += __shfl_xor(tot, o);
+  }
+  if (lane == 0) {
+    s_pre[wv] = pre;
+    s_tot[wv] = tot;
+  }
+  __syncthreads();
+  pre = 0;
+  tot = 0;
+  for (int q = 0; q < kFusedWaves; ++q) {
+    pre += s_pre[q];
+    tot += s_tot[q];
+  }
+  if (s_bad || tot != a.K) {
+    // inconsistent num_draft: this workgroup clears its share of every output
+    const long long gt = (long long)b * kFusedThreads + tid;
+    const long long gs = (long long)a.B * kFusedThreads;
+    for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
+    for (long long i = gt; i < a.K; i += gs) {
+      if (a.p_out) a.p_out[i] = -1.f;
+      if (a.q_out) a.q_out[i] = -1.f;
+    }
+    if (tid == 0) {
+      a.acc_len[b] = -1;
+      if (a.resid_out) a.resid_out[b] = -1.f;
+    }
+    return;
+  }
+  const int k = a.num_draft[b];
+  const int g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
+  const int off = (int)pre;
+  if (tid == 0) {
+    ReqInfo r;
+    r.off = off;
+    r.k = k;
+    r.greedy = g;
+    r.a = 0;
+    r.kind = KIND_NONE;
+    r.y = -1;
+    r.trow = -1;
+    r.drow = -1;
+    r.Mp = r.Mq = 0.f;
+    r.pad0 = r.pad1 = 0;
+    r.Sp = r.Sq = 0.0;
+    a.ws.req[b] = r;
+  }
+  // row statistics: k + 1 target rows, then the k draft rows of a stochastic request
+  using Elem = typename L::Elem;
+  const Elem* tgt = static_cast<const Elem*>(a.target);
+  const Elem* drf = static_cast<const Elem*>(a.draft);
+  const int n_rows = k + 1 + (g ? 0 : k);
+  const int n_units = n_rows * a.nseg;
+  for (int u = wv; u < n_units; u += kFusedWaves) {
+    const int r = u / a.nseg;
+    const int seg = u - r * a.nseg;
+    const bool is_draft = r > k;
+    const int row = is_draft ? off + (r - k - 1) : off + b + r;
+    const int s0 = seg * a.seg;
+    const int s1 = min(s0 + a.seg, a.V);
+    const Elem* base = is_draft ? drf + (int64_t)row * a.dld : tgt + (int64_t)row * a.tld;
+    Partial* out = (is_draft ? a.ws.pd : a.ws.pt) + (int64_t)row * a.nseg + seg;
+    if (g)
+      argmax_unit<L, kFusedUnroll>(base, s0, s1, lane, out);
+    else
+      softmax_unit<L, kFusedUnroll>(base, s0, s1, lane, a, out);
+  }
+  __syncthreads();
+  if (wv == 0) decide_request<L>(a, b, lane, false);
+  __syncthreads();
+  const ReqInfo R = a.ws.req[b];
+  if (R.kind == KIND_RESID) {
+    const Elem* tp = tgt + (int64_t)R.trow * a.tld;
+    const Elem* dp = drf + (int64_t)R.drow * a.dld;
+    const ResidW fw = resid_weights(R, a);
+    for (int seg = wv; seg < a.nrseg; seg += kFusedWaves) {
+      const int s0 = seg * a.rseg;
+      const int s1 = min(s0 + a.rseg, a.V);
+      const double t = resid_unit<L, kFusedUnroll>(tp, dp, fw, R.y, s0, s1, lane);
+      if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = t;
+    }
+    __syncthreads();
+  }
+  finalize_request<L>(a, b, sh);
 }
 
 // ------------------------------------------------------------------ early exit
@@ -1766,6 +1926,12 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
 
 thread_local void* g_ev_begin = nullptr;
 thread_local void* g_ev_end = nullptr;
+thread_local int g_launch_plan = 0;   // 0 automatic, 1 multi-kernel, 2 single launch
+
+// Logit bytes up to which a batch runs as one launch (one workgroup per
+// request): below this the five-kernel path is bound by launch latency.
+constexpr long long kFusedMaxBytes = 48ll << 20;
+constexpr int kFusedMaxRequests = 2048;
 
 std::atomic<int> g_cu_count[64];
 
@@ -1806,6 +1972,13 @@ int resident_blocks(std::atomic<int>* cache, Kern kern, int dev) {
   n = std::min(n, kBlocksPerCU);
   if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+template <class L>
+void launch_fused(const Args& a, hipStream_t st) {
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
+  k_fused<L><<<a.B, kFusedThreads, 0, st>>>(a);
+  if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
 }
 
 template <class L>
@@ -1942,12 +2115,21 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
       if (vec) launch_early_exit<BF16>(a, st, dev, sample);
       else launch_early_exit<Scalar<BF16>>(a, st, dev, sample);
     }
-  } else if (bt->dtype == SV_F32) {
-    if (vec) launch_all<F32>(a, st, dev, sample);
-    else launch_all<Scalar<F32>>(a, st, dev, sample);
   } else {
-    if (vec) launch_all<BF16>(a, st, dev, sample);
-    else launch_all<Scalar<BF16>>(a, st, dev, sample);
+    // one launch for small batches (bytes bounded by all target rows plus a
+    // draft row per drafted token)
+    const long long bytes = (2 * K + B) * V * es;
+    const bool fused = g_launch_plan == 2 ||
+                       (g_launch_plan == 0 && bytes <= kFusedMaxBytes && B <= kFusedMaxRequests);
+    if (bt->dtype == SV_F32) {
+      if (fused) vec ? launch_fused<F32>(a, st) : launch_fused<Scalar<F32>>(a, st);
+      else if (vec) launch_all<F32>(a, st, dev, sample);
+      else launch_all<Scalar<F32>>(a, st, dev, sample);
+    } else {
+      if (fused) vec ? launch_fused<BF16>(a, st) : launch_fused<Scalar<BF16>>(a, st);
+      else if (vec) launch_all<BF16>(a, st, dev, sample);
+      else launch_all<Scalar<BF16>>(a, st, dev, sample);
+    }
   }
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
   return SV_OK;
@@ -2133,6 +2315,12 @@ extern "C" int32_t spec_verify_accept_stats(const int32_t* accepted_len, const i
   k_accept_stats<<<1, kStatsThreads, lds, static_cast<hipStream_t>(stream)>>>(
       accepted_len, num_draft, B, max_pos, out);
   if (hipGetLastError() != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+extern "C" int32_t spec_verify_set_launch_plan(int32_t plan) {
+  if (plan < 0 || plan > 2) return SV_ERR_INVALID_ARG;
+  g_launch_plan = plan;
   return SV_OK;
 }
 

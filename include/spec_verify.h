@@ -269,6 +269,14 @@ int32_t spec_verify_gather_rows(int32_t dtype, int32_t V, const void* src, int64
                                 int32_t src_rows, const int32_t* index, const int32_t* count,
                                 int32_t max_rows, void* dst, int64_t dst_ld, void* stream);
 
+/* Launch plan of spec_verify_greedy / spec_verify_sample for calls made from
+ * the calling thread: 0 = automatic (default: one launch, one workgroup per
+ * request, when the logit rows of the call total at most 48 MiB and B <= 2048;
+ * otherwise the multi-kernel pipeline), 1 = always the multi-kernel pipeline,
+ * 2 = always the single launch.  Both plans run the same arithmetic and return
+ * the same bits.  Thread-local; SV_ERR_INVALID_ARG for other values. */
+int32_t spec_verify_set_launch_plan(int32_t plan);
+
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
  * before and ev_end just after the row-statistics kernel (for the early-exit

@@ -282,3 +282,10 @@ def test_adaptive_and_gather_host_validation(sv):
     assert g(1, 100, FAKE, 100, 4, FAKE, FAKE, -1, FAKE, 100, None) == INV
     assert g(1, 100, FAKE + 1, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
     assert g(1, 100, FAKE, 100, 4, FAKE, FAKE, 0, FAKE, 100, None) == sv.SV_OK   # nothing to copy
+
+
+def test_launch_plan_values(sv):
+    for bad in (-1, 3, 99):
+        assert sv._lib.spec_verify_set_launch_plan(bad) == sv.SV_ERR_INVALID_ARG
+    for ok in (1, 2, 0):
+        assert sv._lib.spec_verify_set_launch_plan(ok) == sv.SV_OK
