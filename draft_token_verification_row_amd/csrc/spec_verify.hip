@@ -944,10 +944,11 @@ __device__ __forceinline__ void unit_weights(const typename L::Elem* tp, const t
 
 // Rescan one unit of PER * kBlock ids: thread t (< kBlock) sums the weights of
 // its PER ids in ascending order, a block-wide exclusive scan of those sums
-// locates the crossing thread, which walks its ids again.  In a block larger
-// than kBlock the extra threads take part in the barriers only, so the result
-// is the same for any block size.
-template <class L, int PER, class WF>
+// locates the crossing thread, which walks its ids again.  KEEP holds the
+// weights in registers for that walk; otherwise they are recomputed (same
+// values, fewer registers).  In a block larger than kBlock the extra threads
+// take part in the barriers only, so the result is the same for any block size.
+template <class L, int PER, bool KEEP, class WF>
 __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* dp, int s0,
                            int s1, int y, const WF& wf, double before, double thr, int fallback,
                            double* s_wave, int* s_owner) {
@@ -958,6 +959,7 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
   const int wv = tid >> 6;
   const bool active = tid < kBlock;
   const int v0 = s0 + tid * PER;
+  float keep[KEEP ? PER : 1];
   double ts = 0.0;
   if (active) {
 #pragma unroll
@@ -965,9 +967,21 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
       float w[E];
       unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
 #pragma unroll
-      for (int e = 0; e < E; ++e) ts += (double)w[e];
+      for (int e = 0; e < E; ++e) {
+        ts += (double)w[e];
+        if constexpr (KEEP) keep[c * E + e] = w[e];
+      }
     }
   }
+  // weights of chunk c for the walks below
+  auto chunk = [&](int c, float* w) {
+    if constexpr (KEEP) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[e] = keep[c * E + e];
+    } else {
+      unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
+    }
+  };
   const double incl_w = wave_incl_scan(ts, lane);
   if (active && lane == kWave - 1) s_wave[wv] = incl_w;
   if (tid == 0) *s_owner = INT_MAX;
@@ -991,9 +1005,10 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
     owner = *s_owner;
     if (tid == owner) {
       int tok = -1;
+#pragma unroll
       for (int c = 0; c < PER / E; ++c) {
         float w[E];
-        unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
+        chunk(c, w);
 #pragma unroll
         for (int e = 0; e < E; ++e)
           if (w[e] > 0.f) tok = v0 + c * E + e;
@@ -1005,9 +1020,10 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
   if (tid != owner) return -2;
   double cum = excl;
   int tok = -1, last = -1;
+#pragma unroll
   for (int c = 0; c < PER / E; ++c) {
     float w[E];
-    unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
+    chunk(c, w);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       cum += (double)w[e];
@@ -1024,8 +1040,9 @@ struct FinalizeShared {
   int unit, mode, fallback, owner;
 };
 
-// Correction or bonus draw of request b by one block of >= kBlock threads.
-template <class L>
+// Correction or bonus draw of request b by one block of >= kBlock threads
+// (KEEP: see rescan_unit).
+template <class L, bool KEEP>
 __device__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
   using Elem = typename L::Elem;
   constexpr int PER_S = kSegBytes / (int)sizeof(Elem) / kBlock;    // k_stats unit
@@ -1070,13 +1087,14 @@ __device__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
     const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
     const int s0 = sh.unit * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
-    tok = rescan_unit<L, PER_R>(tp, dp, s0, s1, R.y, resid_weights(R, a), sh.before, sh.thr,
-                                sh.fallback, sh.wave, &sh.owner);
+    tok = rescan_unit<L, PER_R, KEEP>(tp, dp, s0, s1, R.y, resid_weights(R, a), sh.before,
+                                      sh.thr, sh.fallback, sh.wave, &sh.owner);
   } else {
     const int s0 = sh.unit * a.seg;
     const int s1 = min(s0 + a.seg, a.V);
-    tok = rescan_unit<L, PER_S>(tp, (const Elem*)nullptr, s0, s1, -1, target_weights(R, a),
-                                sh.before, sh.thr, sh.fallback, sh.wave, &sh.owner);
+    tok = rescan_unit<L, PER_S, KEEP>(tp, (const Elem*)nullptr, s0, s1, -1,
+                                      target_weights(R, a), sh.before, sh.thr, sh.fallback,
+                                      sh.wave, &sh.owner);
   }
   if (tok != -2) {
     a.out[R.trow] = tok;
@@ -1089,7 +1107,7 @@ template <class L>
 __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
   __shared__ FinalizeShared sh;
   if (a.ws.hdr->error) return;
-  finalize_request<L>(a, blockIdx.x, sh);
+  finalize_request<L, true>(a, blockIdx.x, sh);
 }
 
 // ------------------------------------------------------------------ single-launch path
@@ -1208,7 +1226,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
     }
     __syncthreads();
   }
-  finalize_request<L>(a, b, sh);
+  finalize_request<L, false>(a, b, sh);
 }
 
 // ------------------------------------------------------------------ early exit
