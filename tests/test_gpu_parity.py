@@ -256,12 +256,12 @@ def test_full_size_sampled(cfg):
 
 
 def test_monte_carlo_distribution_on_gpu():
-    """One batch of many requests over the same small rows, fresh drafts y ~ q and
+    """One batch of 10^6 requests over the same small rows, fresh drafts y ~ q and
     fresh uniforms: committed-token and accepted-length frequencies match the
     closed forms of the method's guarantee (every cell within 5 sigma)."""
     import scipy.special
     rng = np.random.default_rng(2024)
-    V, k, N, T = 8, 3, 200000, 0.9
+    V, k, N, T = 8, 3, 1000000, 0.9
     z = rng.normal(0, 1.5, size=(k + 1, V))
     d = z[:k] + rng.normal(0, 1.0, size=(k, V))
     z32, d32 = z.astype(np.float32), d.astype(np.float32)
