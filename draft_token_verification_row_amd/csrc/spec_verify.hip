@@ -1926,7 +1926,9 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   if (K + B >= (1ll << 29)) return false;
   const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
   const long long nrseg = (V + kRSegMinElems - 1) / kRSegMinElems;
-  if ((2 * K + B) * nseg >= (1ll << 31) || B * nrseg >= (1ll << 31)) return false;
+  // unit counts are 32-bit in the kernels; an early-exit round can list row
+  // units and residual units together
+  if ((2 * K + B) * nseg + B * nrseg >= (1ll << 31)) return false;
   size_t o = 0;
   z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
   z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);

@@ -63,6 +63,10 @@ def test_workspace_sizes(sv):
     assert 0 < a < b and a < c
     # the largest workload needs a few MB, not a copy of the logits
     assert sv.spec_verify_workspace_bytes(512, 3584, 262144) < 16 << 20
+    # row units and residual units of one early-exit round together must fit
+    # a 32-bit count, even when each alone does (V = 2^28: 32768 / 131072 units)
+    assert sv.spec_verify_workspace_bytes(10000, 10000, 1 << 28) == 0
+    assert sv.spec_verify_workspace_bytes(5000, 10000, 1 << 28) > 0
 
 
 FAKE = 1 << 20   # never dereferenced: every call below fails a host check first
