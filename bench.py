@@ -36,13 +36,19 @@ sys.path.insert(0, ROOT)
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (1× MI355X)"
 PEAK_HBM_GBS = 8000.0
 WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "tree": "tree", "adaptive": "adaptive"}
-SRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc", "spec_verify.hip")
+CSRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 over the library sources (name and bytes of each csrc file, sorted)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 class HipEvents:

@@ -1,19 +1,22 @@
 """Compile the HIP library libspecverify.so in-tree, for gfx950 only."""
 from __future__ import annotations
 
+import glob
 import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "spec_verify.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRCS = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
 
 HIP_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",                       # rounding exactly as written
     "-Xarch_device", "-fno-honor-nans",        # logits carry no NaN (documented); drops max canonicalisation
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -28,9 +31,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, SRC, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -38,11 +39,24 @@ def build(verbose: bool = True, extra_flags=()) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
     # keep only real diagnostics (the host pass does not know the gfx feature flag)
-    noise = "packed-fp32-ops"
-    warn = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l
+    warn = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
+                     if "packed-fp32-ops" not in l
                      and "is not a recognized feature for this target" not in l)
     if verbose and warn.strip():
         print(warn)
+
+
+def build(verbose: bool = True, extra_flags=()) -> str:
+    """Compile every csrc/*.hip (in parallel) and link libspecverify.so."""
+    objs = [os.path.join(CSRC, os.path.basename(src)[:-4] + ".o") for src in SRCS]
+    cmds = [[hipcc(), *HIP_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+            for src, obj in zip(SRCS, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 4)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    for o in objs:
+        os.remove(o)
     os.replace(tmp, LIB)
     return LIB
 

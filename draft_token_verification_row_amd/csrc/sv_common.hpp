@@ -1,0 +1,429 @@
+// sv_common.hpp - pieces shared by the kernels of libspecverify (gfx950):
+// workspace records, the element loaders, the per-unit row statistics
+// (softmax partials and argmax partials over one slice of a logit row), the
+// row-statistics kernel k_stats, and host helpers.  Included once by each
+// translation unit of the library; everything but the shared host state
+// below has internal linkage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
+#include "spec_verify.h"
+
+namespace svk {
+// Host state shared by every translation unit (one copy per thread).
+inline thread_local void* g_ev_begin = nullptr;   // profile events (spec_verify_set_profile_events)
+inline thread_local void* g_ev_end = nullptr;
+inline thread_local int g_launch_plan = 0;        // 0 automatic, 1 multi-kernel, 2 single launch
+}  // namespace svk
+
+namespace {
+
+using svk::g_ev_begin;
+using svk::g_ev_end;
+using svk::g_launch_plan;
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+#ifndef SV_UNROLL
+#define SV_UNROLL 2
+#endif
+#ifndef SV_SEG_BYTES
+#define SV_SEG_BYTES 32768
+#endif
+constexpr int kUnroll = SV_UNROLL;       // 16-byte loads in flight per lane per row
+#ifndef SV_ROUND_UNROLL
+#define SV_ROUND_UNROLL 4
+#endif
+// early-exit rounds: same per-lane chunk order (so the same partials bit for
+// bit), more loads in flight for the small late rounds
+constexpr int kRoundUnroll = SV_ROUND_UNROLL;
+#ifndef SV_RESID_UNROLL
+#define SV_RESID_UNROLL 4
+#endif
+constexpr int kResidUnroll = SV_RESID_UNROLL;   // k_resid: loads in flight per lane per row
+constexpr int kSegBytes = SV_SEG_BYTES;  // one unit = 32 KiB of one logit row
+constexpr int kSegMinElems = kSegBytes / 4;
+constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
+constexpr int kTreeSegBytes = 4096; // early-exit tree rounds: 4 KiB units (few rows per round)
+constexpr int kRSegMinElems = kRSegBytes / 4;
+constexpr int kBlocksPerCU = 8;      // 32 wavefronts per CU
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxEarlyExitRounds = 4096;   // bound on max_k (two launches per round)
+
+constexpr uint32_t kDraftBit = 1u << 30;
+constexpr uint32_t kGreedyBit = 1u << 29;
+constexpr uint32_t kRowMask = kGreedyBit - 1u;
+
+enum Kind : int { KIND_NONE = 0, KIND_RESID = 1, KIND_BONUS = 2, KIND_INVALID = 3 };
+enum DrawMode : int { DRAW_RESID = 0, DRAW_FROM_P = 1 };
+
+struct Partial {      // one unit of one row
+  double s;           // sum of exp2((z - m) * c) over the unit (softmax rows)
+  float m;            // max logit of the unit
+  int idx;            // lowest id attaining m (greedy rows)
+};
+
+struct ReqInfo {      // per request; plan fills off/k/greedy, decide the rest
+  int off, k, greedy, a;
+  int kind, y, trow, drow;
+  float Mp, Mq;
+  int pad0, pad1;
+  double Sp, Sq;
+};
+
+struct Header {
+  int error;
+  int n_rows;
+  int n_units;
+  int n_resid;
+  int n_rows3[3];     // early-exit rounds: rows listed for a round (three lists in rotation)
+  int n_res3[3];      // early-exit rounds: residual sweeps listed for a round
+  int n_alive3[3];    // early-exit rounds: requests deciding a position in the round
+  int pad[51];
+};
+
+struct Workspace {
+  Header* hdr;
+  ReqInfo* req;
+  uint32_t* rowdesc;   // [2K + B]
+  int* resid_list;     // [B]
+  Partial* pt;         // [(K + B) * nseg]
+  Partial* pd;         // [K * nseg]
+  double* rp;          // [B * nrseg]
+  uint32_t* rows_r;    // [3][2B]    early-exit rounds: row descriptors
+  int* res_r;          // [3][B]     early-exit rounds: requests whose residual is swept
+  int* alive;          // [3][B]     early-exit rounds: requests deciding a position
+};
+
+struct Args {
+  int B, K, V, nseg, seg, nrseg, rseg;
+  int force_greedy;
+  int64_t tld, dld;
+  const void* target;
+  const void* draft;
+  const int* num_draft;
+  const int* tokens;
+  const uint8_t* gmask;
+  const float* u_accept;
+  const float* u_final;
+  int* acc_len;
+  int* out;
+  float* p_out;
+  float* q_out;
+  float* resid_out;
+  float c_hi, c_lo;    // log2(e)/T split into two fp32 constants, c_lo > 0
+  double c64, T64;
+  const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
+  const int* rowcount;       // number of rows in rowlist
+  int ee_round;              // early-exit round, -1 on the all-rows path
+  int max_k;                 // early-exit: bound on every num_draft[b] (trees: on every depth)
+  const int* parent;         // token trees: [N] local parent index
+  int* path;                 // token trees: [N] walked node indices
+  Workspace ws;
+};
+
+// ------------------------------------------------------------------ element access
+// load():    ordinary 16-byte load (rescans of a single unit, gathers).
+// stream():  16-byte nontemporal load for data read once per call; it keeps the
+//            streamed logits from displacing other lines and measured faster on
+//            gfx950 for read-once sweeps.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct F32 {
+  using Elem = float;
+  static constexpr int E = 4;
+  using Raw = float4;
+  __device__ static __forceinline__ Raw load(const Elem* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+  __device__ static __forceinline__ Raw stream(const Elem* p) {
+    const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+  }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
+    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+  }
+  __device__ static __forceinline__ float one(const Elem* p) { return *p; }
+};
+
+struct BF16 {
+  using Elem = uint16_t;
+  static constexpr int E = 8;
+  using Raw = uint4;
+  __device__ static __forceinline__ Raw load(const Elem* p) {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+  __device__ static __forceinline__ Raw stream(const Elem* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+  }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) {
+    v[0] = __uint_as_float(r.x << 16); v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16); v[3] = __uint_as_float(r.y & 0xffff0000u);
+    v[4] = __uint_as_float(r.z << 16); v[5] = __uint_as_float(r.z & 0xffff0000u);
+    v[6] = __uint_as_float(r.w << 16); v[7] = __uint_as_float(r.w & 0xffff0000u);
+  }
+  __device__ static __forceinline__ float one(const Elem* p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+};
+
+// Unaligned rows: one element per "chunk", plain scalar loads.
+template <class D>
+struct Scalar {
+  using Elem = typename D::Elem;
+  static constexpr int E = 1;
+  using Raw = float;
+  __device__ static __forceinline__ Raw load(const Elem* p) { return D::one(p); }
+  __device__ static __forceinline__ Raw stream(const Elem* p) { return D::one(p); }
+  __device__ static __forceinline__ void unpack(const Raw& r, float* v) { v[0] = r; }
+  __device__ static __forceinline__ float one(const Elem* p) { return D::one(p); }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp((z - m)/T) = exp2(d * c) with d = z - m and c = c_hi + c_lo.
+__device__ __forceinline__ float scaled_exp(float d, float c_hi, float c_lo) {
+  return fast_exp2(fmaf(d, c_hi, d * c_lo));
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Visit the unit [s0, s1) of one row, chunk by chunk, in increasing id order
+// per lane.  f(v, first_id, count) receives E values (padding = -inf).
+template <class L, int U, class F>
+__device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, int s1,
+                                         int lane, F& f) {
+  constexpr int E = L::E;
+  const int n = s1 - s0;
+  const int nchunk = n / E;
+  const typename L::Elem* p = row + s0;
+  constexpr int per_it = kWave * U;
+  const int nit = nchunk / per_it;
+  int c = lane;
+  for (int it = 0; it < nit; ++it, c += per_it) {
+    typename L::Raw r[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      float v[E];
+      L::unpack(r[j], v);
+      f(v, s0 + (c + j * kWave) * E, E);
+    }
+  }
+  for (; c < nchunk; c += kWave) {
+    float v[E];
+    L::unpack(L::stream(p + (size_t)c * E), v);
+    f(v, s0 + c * E, E);
+  }
+  const int tail0 = nchunk * E;
+  if (lane < n - tail0) {
+    float v[E];
+    v[0] = L::one(p + tail0 + lane);
+#pragma unroll
+    for (int e = 1; e < E; ++e) v[e] = -INFINITY;
+    f(v, s0 + tail0 + lane, 1);
+  }
+}
+
+template <int E>
+struct SoftmaxAcc {
+  float m;
+  float s[E];
+  float c_hi, c_lo;
+  __device__ __forceinline__ void operator()(const float* v, int, int) {
+    float cm = v[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
+    if (cm > m) {                    // rare after the first chunks
+      const float f = scaled_exp(m - cm, c_hi, c_lo);
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[e] *= f;
+      m = cm;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] += scaled_exp(v[e] - m, c_hi, c_lo);
+  }
+};
+
+template <int E>
+struct ArgmaxAcc {
+  float best;
+  int idx;
+  __device__ __forceinline__ void operator()(const float* v, int id0, int cnt) {
+    float cm = v[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
+    if (cm > best) {                 // ids only grow within a lane: strict > keeps the lowest
+      int hit = 0;
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e)
+        if (v[e] == cm) hit = e;
+      if (hit < cnt) {
+        best = cm;
+        idx = id0 + hit;
+      }
+    }
+  }
+};
+
+template <class L, int U = kUnroll>
+__device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
+                             const Args& a, Partial* out) {
+  SoftmaxAcc<L::E> acc;
+  acc.m = -FLT_MAX;
+  acc.c_hi = a.c_hi;
+  acc.c_lo = a.c_lo;
+#pragma unroll
+  for (int e = 0; e < L::E; ++e) acc.s[e] = 0.f;
+  for_unit<L, U>(row, s0, s1, lane, acc);
+  float sl = 0.f;
+#pragma unroll
+  for (int e = 0; e < L::E; ++e) sl += acc.s[e];
+  const float mw = wave_max(acc.m);
+  const float f = scaled_exp(acc.m - mw, a.c_hi, a.c_lo);
+  const double sw = wave_sum((double)sl * (double)f);
+  if (lane == 0) {
+    Partial p;
+    p.s = sw;
+    p.m = mw;
+    p.idx = 0;
+    *out = p;
+  }
+}
+
+template <class L, int U = kUnroll>
+__device__ void argmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
+                            Partial* out) {
+  ArgmaxAcc<L::E> acc;
+  acc.best = -INFINITY;
+  acc.idx = INT_MAX;
+  for_unit<L, U>(row, s0, s1, lane, acc);
+  float b = acc.best;
+  int i = acc.idx;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float ob = __shfl_xor(b, o);
+    const int oi = __shfl_xor(i, o);
+    if (ob > b || (ob == b && oi < i)) {
+      b = ob;
+      i = oi;
+    }
+  }
+  if (lane == 0) {
+    Partial p;
+    p.s = 0.0;
+    p.m = b;
+    p.idx = i;
+    *out = p;
+  }
+}
+
+// ------------------------------------------------------------------ block scans
+__device__ __forceinline__ long long wave_incl_scan_ll(long long x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// ------------------------------------------------------------------ k_stats
+// Persistent grid; wavefront gw takes units gw, gw + W, ...  The descriptor of
+// the next unit is fetched while the current one streams.
+template <class L>
+__global__ __launch_bounds__(kBlock) void k_stats(Args a) {
+  using Elem = typename L::Elem;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int W = gridDim.x * kWavesPerBlock;
+  const int n_units = *a.rowcount * a.nseg;
+  const Elem* tgt = static_cast<const Elem*>(a.target);
+  const Elem* drf = static_cast<const Elem*>(a.draft);
+  uint32_t next = (gw < n_units) ? a.rowlist[gw / a.nseg] : 0u;
+  for (int u = gw; u < n_units; u += W) {
+    const uint32_t desc = next;
+    const int ri = u / a.nseg;
+    const int seg = u - ri * a.nseg;
+    if (u + W < n_units) next = a.rowlist[(u + W) / a.nseg];
+    const int row = (int)(desc & kRowMask);
+    const bool is_draft = (desc & kDraftBit) != 0;
+    const bool greedy = (desc & kGreedyBit) != 0;
+    const int s0 = seg * a.seg;
+    const int s1 = min(s0 + a.seg, a.V);
+    const Elem* base = is_draft ? drf + (int64_t)row * a.dld : tgt + (int64_t)row * a.tld;
+    Partial* out = (is_draft ? a.ws.pd : a.ws.pt) + (int64_t)row * a.nseg + seg;
+    if (greedy)
+      argmax_unit<L>(base, s0, s1, lane, out);
+    else
+      softmax_unit<L>(base, s0, s1, lane, a, out);
+  }
+}
+
+// ------------------------------------------------------------------ host helpers
+size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
+
+std::atomic<int> g_cu_count[64];
+
+int cu_count(int dev) {
+  if (dev >= 0 && dev < 64) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    c = 256;
+  if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  return c;
+}
+
+void split_constant(double T, float* hi, float* lo, double* c64) {
+  const double c = 1.4426950408889634 / T;   // log2(e) / T
+  float h = (float)c;
+  if ((double)h > c) h = nextafterf(h, 0.f);  // round toward zero so that c_lo >= 0
+  float l = (float)(c - (double)h);
+  if (!(l >= 1e-30f)) l = 1e-30f;             // keep c_lo > 0: -inf * c_lo stays -inf
+  *hi = h;
+  *lo = l;
+  *c64 = c;
+}
+
+template <class Kern>
+int resident_blocks(std::atomic<int>* cache, Kern kern, int dev) {
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kBlock, 0) != hipSuccess || n <= 0)
+    n = 1;
+  n = std::min(n, kBlocksPerCU);
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace
