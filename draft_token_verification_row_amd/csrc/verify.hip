@@ -1264,6 +1264,8 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   if (sample) {
     if (!u_final) return SV_ERR_INVALID_ARG;
     if (!(temperature > 0.f) || !isfinite(temperature)) return SV_ERR_INVALID_ARG;
+    // exp((z - m)/T) runs as exp2((z - m) * log2(e)/T) with that constant in fp32
+    if (!(1.4426950408889634 / (double)temperature < (double)FLT_MAX)) return SV_ERR_INVALID_ARG;
     if (K > 0 && (!u_accept || !bt->draft)) return SV_ERR_INVALID_ARG;
   }
   if (need_draft) {

@@ -106,7 +106,9 @@ int32_t spec_verify_greedy(const sv_batch_t* batch,
 /* Stochastic verification (chzhyang section 1: acceptance probability
  * min(1, p/q), residual [p - q]_+ at the first rejection, bonus from the
  * target), optionally mixed with greedy requests.
- *   temperature   > 0 and finite; applied to target and draft logits alike.
+ *   temperature   > 0 and finite, with log2(e)/temperature representable in
+ *                 fp32 (temperature >= about 4.3e-39); applied to target and
+ *                 draft logits alike.
  *   greedy_mask   device [B] or NULL; a non-zero byte makes request b greedy
  *                 (its draft rows, u_accept and u_final are then not read).
  *   u_accept      device [K] uniforms in [0,1), one per draft position.

@@ -108,7 +108,7 @@ def test_host_validation_rejects_bad_arguments(sv):
     assert _sample(sv, _batch(sv, draft_tokens=None)) == INV
     assert _sample(sv, _batch(sv, target=FAKE + 2)) == INV          # fp32 rows must be 4-byte aligned
     assert _sample(sv, _batch(sv, dtype=1, target=FAKE + 1)) == INV  # bf16 rows 2-byte aligned
-    for T in (0.0, -1.0, float("nan"), float("inf")):
+    for T in (0.0, -1.0, float("nan"), float("inf"), 1e-39, 1e-45):
         assert _sample(sv, _batch(sv), T=T) == INV, T
     assert _sample(sv, _batch(sv), ua=None) == INV
     assert _sample(sv, _batch(sv), uf=None) == INV

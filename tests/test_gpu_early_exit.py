@@ -150,7 +150,7 @@ def test_early_exit_repeat_and_stream():
             assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_early_exit_full_size(cfg):
     """Full workload shape in the launch configuration the benchmark times:
     bit-identical to the all-rows path, and a seeded sample against the oracle."""

@@ -99,6 +99,17 @@ def test_golden_examples_on_gpu():
         assert got["out_tokens"][:n].tolist() == c["committed"], (c, got)
 
 
+@pytest.mark.parametrize("T", [1e-20, 1e-3, 50.0, 1e6])
+def test_extreme_temperatures(T):
+    """Temperatures far from 1 (near-argmax and near-uniform distributions)."""
+    batch = synth.make_batch(5, DEV, B=24, V=4099)
+    batch.temperature = float(np.float32(T))
+    got = run_hip(batch)
+    ref = run_oracle(batch)
+    near = compare(batch, got, ref, f"T={T}")
+    assert near <= 1
+
+
 def test_masked_vocabulary_columns():
     batch = synth.make_batch(5, DEV, B=20, V=40000)
     batch.target[:, -3000:] = float("-inf")
