@@ -61,6 +61,10 @@ class HipEvents:
                                                  ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def record(self, ev, stream):
+        assert self.lib.hipEventRecord(ev, stream) == 0
 
     def create(self, n):
         evs = []
@@ -79,6 +83,20 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.lib.hipEventDestroy(e)
+
+
+def host_cpu() -> str:
+    """CPU model and logical core count of the machine the oracle runs on."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}, {os.cpu_count()} logical cores (the oracle used 1)"
 
 
 def cpu_baseline(batch, min_seconds: float, max_requests: int):
@@ -102,7 +120,7 @@ def cpu_baseline(batch, min_seconds: float, max_requests: int):
         rows += sub.K + sub.B + int(sub.num_draft[sub.greedy == 0].sum()) if sub.temperature else sub.K + sub.B
         done_req += len(reqs)
     return dict(value=done_pos / t_total if t_total > 0 else None, unit="verified draft positions/s",
-                cores=1, kind="oracle",
+                cores=1, kind="oracle", host=host_cpu(),
                 sample=f"first {done_req} of {batch.B} requests ({done_pos} positions, {rows} logit rows), "
                        f"{t_total:.1f} s of fp64 NumPy on one host core")
 
@@ -123,7 +141,7 @@ def cpu_baseline_tree(tb, min_seconds: float):
         nodes += int(sub.num_nodes.sum()) - sub.B
         done += len(reqs)
     return dict(value=nodes / t_total if t_total > 0 else None, unit="verified draft positions/s",
-                cores=1, kind="oracle",
+                cores=1, kind="oracle", host=host_cpu(),
                 sample=f"first {done} of {tb.B} trees ({nodes} draft nodes), {t_total:.1f} s of "
                        f"NumPy on one host core")
 
@@ -340,6 +358,9 @@ def main():
     ap.add_argument("--early-exit", action="store_true",
                     help="headline = the early-exit entry points (rows read only up to each cut); "
                          "the all-rows path is then reported under other_path, and vice versa")
+    ap.add_argument("--mall-flush", choices=["auto", "on", "off"], default="auto",
+                    help="write 512 MiB between timed calls so the 256 MB MALL holds no logits "
+                         "(auto: on when one call reads less than 768 MiB)")
     ap.add_argument("--launch-plan", default="auto", choices=["auto", "multi", "single"],
                     help="launch plan of the all-rows entry points (library default: auto)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -417,24 +438,6 @@ def main():
         return
 
     hip = HipEvents()
-
-    def timed(fn, steps):
-        """Wall time per call over `steps` calls, and the mean of the HIP-event
-        interval the library records around its row-statistics launches."""
-        ev_b = hip.create(steps)
-        ev_e = hip.create(steps)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
-            fn()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        sv.spec_verify_set_profile_events(None, None)
-        ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
-        hip.destroy(ev_b + ev_e)
-        return (t1 - t0) / steps, float(np.mean(ms)) / 1e3
-
     es = 4 if batch.dtype == "f32" else 2
     k_np = batch.num_draft.astype(np.int64)
     stoch = np.zeros(batch.B, bool) if greedy_only else (batch.greedy == 0)
@@ -446,7 +449,46 @@ def main():
         a_np = acc.cpu().numpy().astype(np.int64)
         return int((a_np + 1).sum() + np.minimum(a_np + 1, k_np)[stoch].sum())
 
-    step_s, t_stats = timed(call, args.steps)
+    bytes_all = rows_read(False) * batch.V * es
+    flush = args.mall_flush == "on" or (args.mall_flush == "auto" and bytes_all < (768 << 20))
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+
+    def timed(fn, steps):
+        """Per call: GPU time from HIP events around the C-ABI call on its stream
+        (median, p10, p90), and the mean of the interval the library records
+        around its row-statistics launches; plus wall time per call.  With the
+        MALL flush a 512 MiB fill runs between calls, outside the call events."""
+        ev_b, ev_e = hip.create(steps), hip.create(steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if flush:
+                scratch.zero_()
+            sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sv.spec_verify_set_profile_events(None, None)
+        ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
+        hip.destroy(ev_b + ev_e)
+        wall = (t1 - t0) / steps
+        # per-call GPU time in a separate pass (events around each call would
+        # slow the back-to-back loop above)
+        n = min(steps, 50)
+        cb, ce = hip.create(n), hip.create(n)
+        for i in range(n):
+            if flush:
+                scratch.zero_()
+            hip.record(cb[i], sh)
+            fn()
+            hip.record(ce[i], sh)
+        torch.cuda.synchronize()
+        call_ms = np.array([hip.elapsed_ms(cb[i], ce[i]) for i in range(n)])
+        hip.destroy(cb + ce)
+        step = float(np.median(call_ms)) / 1e3 if flush else wall
+        return step, float(np.mean(ms)) / 1e3, call_ms, wall
+
+    step_s, t_stats, call_ms, wall_s = timed(call, args.steps)
     positions = int(batch.num_draft.sum())
     rows = rows_read(ee)
     bytes_stats = rows * batch.V * es
@@ -456,7 +498,7 @@ def main():
     other = make_call(not ee)
     for _ in range(max(args.warmup // 2, 2)):
         assert other() == 0
-    o_step, o_t = timed(other, max(args.steps // 2, 5))
+    o_step, o_t, _, _ = timed(other, max(args.steps // 2, 5))
     o_bytes = rows_read(not ee) * batch.V * es
     call()                      # leave the headline path's outputs in acc/out
     torch.cuda.synchronize()
@@ -492,6 +534,12 @@ def main():
             "path": path(ee),
             "launch_plan": args.launch_plan,
         },
+        "call_gpu_us": {"median": float(np.median(call_ms)) * 1e3,
+                        "p10": float(np.percentile(call_ms, 10)) * 1e3,
+                        "p90": float(np.percentile(call_ms, 90)) * 1e3,
+                        "wall_per_call": wall_s * 1e6,
+                        "timing": ("median of per-call HIP events, 512 MiB MALL flush between calls"
+                                   if flush else "wall clock over back-to-back calls")},
         "rows_per_s": (batch.K + batch.B) / step_s,
         "hbm_gbs_step": bytes_stats / step_s / 1e9,
         "hbm_frac_step": bytes_stats / step_s / 1e9 / PEAK_HBM_GBS,
@@ -504,6 +552,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
+            "traffic_ratio": (traffic / bytes_stats) if traffic else None,
             "algorithmic_bytes_per_launch": bytes_stats,
             "avg_kernel_ms": t_stats * 1e3,
         },
