@@ -36,22 +36,22 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 #ifndef SV_UNROLL
-#define SV_UNROLL 2
+#define SV_UNROLL 1
 #endif
 #ifndef SV_SEG_BYTES
 #define SV_SEG_BYTES 32768
 #endif
-constexpr int kUnroll = SV_UNROLL;       // 16-byte loads in flight per lane per row
+constexpr int kUnroll = SV_UNROLL;       // 16-byte chunks per lane per step of a unit loop
 #ifndef SV_ROUND_UNROLL
-#define SV_ROUND_UNROLL 4
+#define SV_ROUND_UNROLL 2
 #endif
 // early-exit rounds: same per-lane chunk order (so the same partials bit for
 // bit), more loads in flight for the small late rounds
 constexpr int kRoundUnroll = SV_ROUND_UNROLL;
 #ifndef SV_RESID_UNROLL
-#define SV_RESID_UNROLL 4
+#define SV_RESID_UNROLL 1
 #endif
-constexpr int kResidUnroll = SV_RESID_UNROLL;   // k_resid: loads in flight per lane per row
+constexpr int kResidUnroll = SV_RESID_UNROLL;   // k_resid: chunks per lane per row and step
 constexpr int kSegBytes = SV_SEG_BYTES;  // one unit = 32 KiB of one logit row
 constexpr int kSegMinElems = kSegBytes / 4;
 constexpr int kRSegBytes = 8192;    // residual unit = 8 KiB of each of two rows
@@ -122,8 +122,8 @@ struct Args {
   float* p_out;
   float* q_out;
   float* resid_out;
-  float c_hi, c_lo;    // log2(e)/T split into two fp32 constants, c_lo > 0
-  double c64, T64;
+  float c;            // fl(log2(e)/T): the scale of every exponent
+  double c64;         // the same value in fp64
   const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
   const int* rowcount;       // number of rows in rowlist
   int ee_round;              // early-exit round, -1 on the all-rows path
@@ -194,10 +194,16 @@ struct Scalar {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// exp((z - m)/T) = exp2(d * c) with d = z - m and c = c_hi + c_lo.
-__device__ __forceinline__ float scaled_exp(float d, float c_hi, float c_lo) {
-  return fast_exp2(fmaf(d, c_hi, d * c_lo));
-}
+// exp((z - m)/T) as exp2((z - m) * c) with the one fp32 scale c = fl(log2(e)/T):
+// z - m is exact for bf16 logits (and within half an ulp for f32), the product
+// is rounded once, and z <= m keeps the exponent <= 0 for any finite m, so no
+// row can overflow.  Every kernel uses this same c, so all of them see the
+// softmax at the temperature log2(e)/c (within a relative 2^-24 of T).
+__device__ __forceinline__ float scaled_exp(float d, float c) { return fast_exp2(d * c); }
+
+// A softmax row with no mass (every logit -inf) has no distribution; the
+// decision kernels report a request that tests such a row as invalid.
+__device__ __forceinline__ bool row_has_mass(double S) { return S > 0.0; }
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -212,7 +218,11 @@ __device__ __forceinline__ double wave_sum(double x) {
 }
 
 // Visit the unit [s0, s1) of one row, chunk by chunk, in increasing id order
-// per lane.  f(v, first_id, count) receives E values (padding = -inf).
+// per lane.  f(v, first_id, count) receives E values (padding = -inf).  The
+// loop is software-pipelined: the U chunks of the next step are requested
+// before the current U are consumed, so every wavefront keeps loads in flight
+// while it computes.  The per-lane order of the chunks does not depend on U,
+// so the result is the same bit for bit for any U.
 template <class L, int U, class F>
 __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, int s1,
                                          int lane, F& f) {
@@ -223,16 +233,29 @@ __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, in
   constexpr int per_it = kWave * U;
   const int nit = nchunk / per_it;
   int c = lane;
-  for (int it = 0; it < nit; ++it, c += per_it) {
-    typename L::Raw r[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
+  auto consume = [&](const typename L::Raw* r) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       float v[E];
       L::unpack(r[j], v);
       f(v, s0 + (c + j * kWave) * E, E);
     }
+  };
+  if (nit > 0) {
+    typename L::Raw r[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) r[j] = L::stream(p + (size_t)(c + j * kWave) * E);
+    for (int it = 1; it < nit; ++it) {
+      typename L::Raw nx[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) nx[j] = L::stream(p + (size_t)(c + per_it + j * kWave) * E);
+      consume(r);
+#pragma unroll
+      for (int j = 0; j < U; ++j) r[j] = nx[j];
+      c += per_it;
+    }
+    consume(r);
+    c += per_it;
   }
   for (; c < nchunk; c += kWave) {
     float v[E];
@@ -251,21 +274,21 @@ __device__ __forceinline__ void for_unit(const typename L::Elem* row, int s0, in
 
 template <int E>
 struct SoftmaxAcc {
-  float m;
+  float m;             // running maximum of the lane
   float s[E];
-  float c_hi, c_lo;
+  float c;
   __device__ __forceinline__ void operator()(const float* v, int, int) {
     float cm = v[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
     if (cm > m) {                    // rare after the first chunks
-      const float f = scaled_exp(m - cm, c_hi, c_lo);
+      const float f = scaled_exp(m - cm, c);
 #pragma unroll
       for (int e = 0; e < E; ++e) s[e] *= f;
       m = cm;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) s[e] += scaled_exp(v[e] - m, c_hi, c_lo);
+    for (int e = 0; e < E; ++e) s[e] += scaled_exp(v[e] - m, c);
   }
 };
 
@@ -295,8 +318,7 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
                              const Args& a, Partial* out) {
   SoftmaxAcc<L::E> acc;
   acc.m = -FLT_MAX;
-  acc.c_hi = a.c_hi;
-  acc.c_lo = a.c_lo;
+  acc.c = a.c;
 #pragma unroll
   for (int e = 0; e < L::E; ++e) acc.s[e] = 0.f;
   for_unit<L, U>(row, s0, s1, lane, acc);
@@ -304,7 +326,7 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
 #pragma unroll
   for (int e = 0; e < L::E; ++e) sl += acc.s[e];
   const float mw = wave_max(acc.m);
-  const float f = scaled_exp(acc.m - mw, a.c_hi, a.c_lo);
+  const float f = scaled_exp(acc.m - mw, a.c);
   const double sw = wave_sum((double)sl * (double)f);
   if (lane == 0) {
     Partial p;
@@ -401,15 +423,11 @@ int cu_count(int dev) {
   return c;
 }
 
-void split_constant(double T, float* hi, float* lo, double* c64) {
-  const double c = 1.4426950408889634 / T;   // log2(e) / T
-  float h = (float)c;
-  if ((double)h > c) h = nextafterf(h, 0.f);  // round toward zero so that c_lo >= 0
-  float l = (float)(c - (double)h);
-  if (!(l >= 1e-30f)) l = 1e-30f;             // keep c_lo > 0: -inf * c_lo stays -inf
-  *hi = h;
-  *lo = l;
-  *c64 = c;
+// c = fl(log2(e)/T), rounded to nearest; the caller has checked that
+// log2(e)/T < FLT_MAX.
+void set_scale(double T, float* c, double* c64) {
+  *c = (float)(1.4426950408889634 / T);
+  *c64 = (double)*c;
 }
 
 template <class Kern>

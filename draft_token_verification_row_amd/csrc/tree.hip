@@ -307,8 +307,7 @@ int32_t run_tree(const sv_tree_t* tr, int32_t* acc_len, int32_t* path, int32_t* 
   a.acc_len = acc_len;
   a.out = out;
   a.path = path;
-  a.T64 = 1.0;
-  split_constant(1.0, &a.c_hi, &a.c_lo, &a.c64);
+  set_scale(1.0, &a.c, &a.c64);
   a.ws.hdr = reinterpret_cast<Header*>(wb + z.off_hdr);
   a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);
   a.ws.rowdesc = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc);

@@ -33,11 +33,13 @@
 // requests still undecided, residual sweeps of the requests cut at j - 1) and a
 // k_decide_round launch (decides position j), then k_finalize.
 //
-// Numerics.  exp((z - m)/T) is evaluated as exp2((z - m) * c) with
-// c = log2(e)/T split into two fp32 constants (c_hi + c_lo), so the rounding of
-// c does not bias whole rows.  Lane partial sums are fp32 over at most a few
-// dozen terms, combined across lanes, units and rows in fp64.  p(y) and q(y)
-// are formed in fp64 from the exact logit at y.  Greedy argmax is exact
+// Numerics.  Every exponent is exp2((z - m) * c) with one fp32 scale
+// c = fl(log2(e)/T): all kernels compute the softmax at the temperature
+// log2(e)/c, within a relative 2^-24 of T.  Lane partial sums are fp32 over at
+// most a few dozen terms, combined across lanes, units and rows in fp64.  p(y)
+// and q(y) are formed in fp64 as exp2((z_y - M) * c) / S (the product is exact
+// in fp64).  A stochastic row whose logits are all -inf has no distribution:
+// a request that tests such a row reports -1.  Greedy argmax is exact
 // (lexicographic max of (value, -id)).
 #include "sv_common.hpp"
 
@@ -134,12 +136,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
 // ------------------------------------------------------------------ row combines
 // One lane combines the nseg unit partials of one row.  Loads are issued in
 // groups of 16 so that they are in flight together (one group covers a
-// 262144-id bf16 row); unit factors use the same split-constant exp2 as the
-// streaming kernels and accumulate in fp64.
+// 262144-id bf16 row); unit factors use the same scaled exp2 as the streaming
+// kernels and accumulate in fp64.
 constexpr int kCombineGroup = 16;
 
-__device__ void row_softmax(const Partial* P, int nseg, float c_hi, float c_lo, float& M,
-                            double& S) {
+__device__ void row_softmax(const Partial* P, int nseg, float c, float& M, double& S) {
   float m = -FLT_MAX;
   double s = 0.0;
   for (int g0 = 0; g0 < nseg; g0 += kCombineGroup) {
@@ -160,12 +161,12 @@ __device__ void row_softmax(const Partial* P, int nseg, float c_hi, float c_lo, 
 #pragma unroll
     for (int j = 0; j < kCombineGroup; ++j) gm = fmaxf(gm, pm[j]);
     if (gm > m) {
-      s *= (double)scaled_exp(m - gm, c_hi, c_lo);
+      s *= (double)scaled_exp(m - gm, c);
       m = gm;
     }
 #pragma unroll
     for (int j = 0; j < kCombineGroup; ++j)
-      if (ps[j] > 0.0) s += ps[j] * (double)scaled_exp(pm[j] - m, c_hi, c_lo);
+      if (ps[j] > 0.0) s += ps[j] * (double)scaled_exp(pm[j] - m, c);
   }
   M = m;
   S = s;
@@ -212,7 +213,7 @@ __device__ __forceinline__ float logit_at(const void* base, int64_t row, int64_t
 // are in the workspace).  queue: list the request for k_resid when it needs a
 // residual sweep (the single-launch path sweeps it in the same workgroup).
 template <class D>
-__device__ void decide_request(const Args& a, int b, int lane, bool queue) {
+__device__ __forceinline__ void decide_request(const Args& a, int b, int lane, bool queue) {
   const ReqInfo R = a.ws.req[b];
   const int k = R.k;
   const int trow0 = R.off + b;
@@ -224,6 +225,7 @@ __device__ void decide_request(const Args& a, int b, int lane, bool queue) {
   int A = k;
   bool found = false;       // A fixed (a rejection seen, or the bonus row reached)
   bool invalid = false;
+  bool no_mass = false;     // a row at a position <= A has no mass (all -inf)
   float MpA = 0.f, MqA = 0.f;
   double SpA = 0.0, SqA = 0.0;
   int amaxA = INT_MAX;
@@ -249,12 +251,16 @@ __device__ void decide_request(const Args& a, int b, int lane, bool queue) {
       if (g)
         row_argmax(P, nseg, amax);
       else
-        row_softmax(P, nseg, a.c_hi, a.c_lo, M, S);
+        row_softmax(P, nseg, a.c, M, S);
     } else if (upper && !g && i < k) {
-      row_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.c_hi, a.c_lo, M, S);
+      row_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.c, M, S);
     }
     const float Mq = __shfl(M, half + 32);
     const double Sq = __shfl(S, half + 32);
+    const bool own_ok = g || row_has_mass(S);
+    const bool draft_ok = __shfl(own_ok, half + 32);
+    const bool pos_ok = own_ok && (i >= k || draft_ok);    // lanes < 32, positions i <= k
+    const bool was_found = found;
     bool rej = false;
     if (!upper && i < k) {
       if (g) {
@@ -265,9 +271,13 @@ __device__ void decide_request(const Args& a, int b, int lane, bool queue) {
         invalid = true;
         if (a.p_out) a.p_out[drow0 + i] = -1.f;
         if (a.q_out) a.q_out[drow0 + i] = -1.f;
+      } else if (!pos_ok) {
+        rej = true;      // the request is reported invalid (this position is tested)
+        if (a.p_out) a.p_out[drow0 + i] = -1.f;
+        if (a.q_out) a.q_out[drow0 + i] = -1.f;
       } else {
-        const double py = exp(((double)zy - (double)M) / a.T64) / S;
-        const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
+        const double py = exp2(((double)zy - (double)M) * a.c64) / S;
+        const double qy = exp2(((double)dy - (double)Mq) * a.c64) / Sq;
         rej = !((double)a.u_accept[drow0 + i] * qy < py);
         if (a.p_out) a.p_out[drow0 + i] = (float)py;
         if (a.q_out) a.q_out[drow0 + i] = (float)qy;
@@ -280,6 +290,12 @@ __device__ void decide_request(const Args& a, int b, int lane, bool queue) {
     } else if (!found && k < base + 32) {
       found = true;      // A = k, the bonus row lies in this chunk
     }
+    if (!was_found) {    // positions base .. min(A, base + 31) are tested
+      const unsigned long long bad = __ballot(!upper && i <= k && !pos_ok);
+      const unsigned long long tested =
+          found ? ((A - base >= 63) ? ~0ull : ((2ull << (A - base)) - 1ull)) : ~0ull;
+      if (bad & tested) no_mass = true;
+    }
     if (found && A >= base && A < base + 32) {
       const int src = A - base;
       MpA = __shfl(M, src);
@@ -290,8 +306,12 @@ __device__ void decide_request(const Args& a, int b, int lane, bool queue) {
     }
     if (g && found) break;
   }
-  if (__any(invalid)) {
+  if (__any(invalid) || no_mass) {
     for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
+    for (int i = lane; i < k; i += kWave) {
+      if (a.p_out) a.p_out[drow0 + i] = -1.f;
+      if (a.q_out) a.q_out[drow0 + i] = -1.f;
+    }
     if (lane == 0) {
       a.acc_len[b] = -1;
       if (a.resid_out) a.resid_out[b] = -1.f;
@@ -366,18 +386,17 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
 // maxima and fp32 reciprocals of the row sums.  k_resid and k_finalize use
 // these same functions, so both see identical per-id values.
 struct ResidW {
-  float Mp, Mq, ip, iq, c_hi, c_lo;
+  float Mp, Mq, ip, iq, c;
   __device__ __forceinline__ float operator()(float z, float d) const {
-    const float p = scaled_exp(z - Mp, c_hi, c_lo) * ip;
-    const float q = scaled_exp(d - Mq, c_hi, c_lo) * iq;
-    return fmaxf(p - q, 0.f);
+    const float p = scaled_exp(z - Mp, c) * ip;
+    return fmaxf(fmaf(-scaled_exp(d - Mq, c), iq, p), 0.f);
   }
 };
 
 struct TargetW {
-  float Mp, ip, c_hi, c_lo;
+  float Mp, ip, c;
   __device__ __forceinline__ float operator()(float z) const {
-    return scaled_exp(z - Mp, c_hi, c_lo) * ip;
+    return scaled_exp(z - Mp, c) * ip;
   }
 };
 
@@ -387,8 +406,7 @@ __device__ __forceinline__ ResidW resid_weights(const ReqInfo& R, const Args& a)
   w.Mq = R.Mq;
   w.ip = (float)(1.0 / R.Sp);
   w.iq = (float)(1.0 / R.Sq);
-  w.c_hi = a.c_hi;
-  w.c_lo = a.c_lo;
+  w.c = a.c;
   return w;
 }
 
@@ -396,8 +414,7 @@ __device__ __forceinline__ TargetW target_weights(const ReqInfo& R, const Args& 
   TargetW w;
   w.Mp = R.Mp;
   w.ip = (float)(1.0 / R.Sp);
-  w.c_hi = a.c_hi;
-  w.c_lo = a.c_lo;
+  w.c = a.c;
   return w;
 }
 
@@ -427,18 +444,37 @@ __device__ __forceinline__ double resid_unit(const typename L::Elem* tp, const t
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += r[e];
   };
+  // software-pipelined as for_unit: the next U chunks of both rows are
+  // requested before the current ones are consumed
   constexpr int per_it = kWave * U;
   const int nit = nchunk / per_it;
   int c = lane;
-  for (int it = 0; it < nit; ++it, c += per_it) {
+  if (nit > 0) {
     typename L::Raw rt[U], rd[U];
 #pragma unroll
     for (int jj = 0; jj < U; ++jj) {
       rt[jj] = L::stream(tp + s0 + (size_t)(c + jj * kWave) * E);
       rd[jj] = L::stream(dp + s0 + (size_t)(c + jj * kWave) * E);
     }
+    for (int it = 1; it < nit; ++it) {
+      typename L::Raw nt[U], nd[U];
+#pragma unroll
+      for (int jj = 0; jj < U; ++jj) {
+        nt[jj] = L::stream(tp + s0 + (size_t)(c + per_it + jj * kWave) * E);
+        nd[jj] = L::stream(dp + s0 + (size_t)(c + per_it + jj * kWave) * E);
+      }
+#pragma unroll
+      for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
+#pragma unroll
+      for (int jj = 0; jj < U; ++jj) {
+        rt[jj] = nt[jj];
+        rd[jj] = nd[jj];
+      }
+      c += per_it;
+    }
 #pragma unroll
     for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
+    c += per_it;
   }
   for (; c < nchunk; c += kWave)
     chunk(L::stream(tp + s0 + (size_t)c * E), L::stream(dp + s0 + (size_t)c * E), s0 + c * E);
@@ -504,13 +540,13 @@ __device__ __forceinline__ double wave_incl_scan(double x, int lane) {
 struct UnitMass {
   const double* rp;
   const Partial* prow;
-  float Mp, c_hi, c_lo;
+  float Mp, c;
   double invSp;
   bool resid;
   __device__ __forceinline__ double operator()(int s) const {
     if (resid) return rp[s];
     const Partial p = prow[s];
-    return p.s > 0.0 ? p.s * (double)scaled_exp(p.m - Mp, c_hi, c_lo) * invSp : 0.0;
+    return p.s > 0.0 ? p.s * (double)scaled_exp(p.m - Mp, c) * invSp : 0.0;
   }
 };
 
@@ -683,7 +719,7 @@ struct FinalizeShared {
 // Correction or bonus draw of request b by one block of >= kBlock threads
 // (KEEP: see rescan_unit).
 template <class L, bool KEEP>
-__device__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
+__device__ __forceinline__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
   using Elem = typename L::Elem;
   constexpr int PER_S = kSegBytes / (int)sizeof(Elem) / kBlock;    // k_stats unit
   constexpr int PER_R = kRSegBytes / (int)sizeof(Elem) / kBlock;   // k_resid unit
@@ -697,8 +733,7 @@ __device__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
     um.rp = a.ws.rp + (int64_t)b * a.nrseg;
     um.prow = a.ws.pt + (int64_t)R.trow * a.nseg;
     um.Mp = R.Mp;
-    um.c_hi = a.c_hi;
-    um.c_lo = a.c_lo;
+    um.c = a.c;
     um.invSp = 1.0 / R.Sp;
     um.resid = (R.kind == KIND_RESID);
     int mode = um.resid ? DRAW_RESID : DRAW_FROM_P;
@@ -758,7 +793,8 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
 // multi-kernel path, so the results are the same bit for bit.
 constexpr int kFusedThreads = 1024;
 constexpr int kFusedWaves = kFusedThreads / kWave;
-constexpr int kFusedUnroll = 8;
+constexpr int kFusedUnroll = 4;
+constexpr int kFusedResidUnroll = 2;
 
 template <class L>
 __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
@@ -861,7 +897,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
     for (int seg = wv; seg < a.nrseg; seg += kFusedWaves) {
       const int s0 = seg * a.rseg;
       const int s1 = min(s0 + a.rseg, a.V);
-      const double t = resid_unit<L, kFusedUnroll>(tp, dp, fw, R.y, s0, s1, lane);
+      const double t = resid_unit<L, kFusedResidUnroll>(tp, dp, fw, R.y, s0, s1, lane);
       if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = t;
     }
     __syncthreads();
@@ -1019,13 +1055,24 @@ __device__ __forceinline__ void decide_position(const Args& a, int b, int j, int
   } else if (lane == 0 || (lane == 1 && draft_row)) {
     const Partial* P = (lane == 0) ? a.ws.pt + (int64_t)trow * nseg
                                    : a.ws.pd + (int64_t)drow * nseg;
-    row_softmax(P, nseg, a.c_hi, a.c_lo, M, S);
+    row_softmax(P, nseg, a.c, M, S);
   }
   const float Mq = __shfl(M, 1);
   const double Sq = __shfl(S, 1);
   M = __shfl(M, 0);
   S = __shfl(S, 0);
   amax = __shfl(amax, 0);
+  if (!g && !(row_has_mass(S) && (j == k || row_has_mass(Sq)))) {
+    // a tested row without mass: the request reports -1 everywhere, as on the
+    // all-rows path (slots and p, q of earlier positions are reset)
+    for (int i = lane; i <= k; i += kWave) a.out[R.off + b + i] = -1;
+    for (int i = lane; i < k; i += kWave) {
+      if (a.p_out) a.p_out[R.off + i] = -1.f;
+      if (a.q_out) a.q_out[R.off + i] = -1.f;
+    }
+    if (lane == 0) a.acc_len[b] = -1;
+    return;
+  }
   if (j == k) {                         // every draft kept: the final token
     if (g) {
       if (lane == 0) {
@@ -1049,8 +1096,8 @@ __device__ __forceinline__ void decide_position(const Args& a, int b, int j, int
   if (g) {
     rej = (y != amax);
   } else {
-    const double py = exp(((double)zy - (double)M) / a.T64) / S;
-    const double qy = exp(((double)dy - (double)Mq) / a.T64) / Sq;
+    const double py = exp2(((double)zy - (double)M) * a.c64) / S;
+    const double qy = exp2(((double)dy - (double)Mq) * a.c64) / Sq;
     rej = !((double)u * qy < py);
     if (a.p_out) a.p_out[drow] = (float)py;
     if (a.q_out) a.q_out[drow] = (float)qy;
@@ -1301,11 +1348,9 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.q_out = sample ? q_out : nullptr;
   a.resid_out = sample ? resid_out : nullptr;
   if (sample) {
-    a.T64 = (double)temperature;
-    split_constant(a.T64, &a.c_hi, &a.c_lo, &a.c64);
+    set_scale((double)temperature, &a.c, &a.c64);
   } else {
-    a.T64 = 1.0;
-    split_constant(1.0, &a.c_hi, &a.c_lo, &a.c64);
+    set_scale(1.0, &a.c, &a.c64);
   }
   a.ws.hdr = reinterpret_cast<Header*>(wb + z.off_hdr);
   a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);

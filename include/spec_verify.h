@@ -41,10 +41,16 @@
  *   - Device-side input problems are reported in the outputs, never by a
  *     fault: if sum(num_draft) != K or some num_draft[b] < 0, every
  *     accepted_len is -1 and every output slot is -1; a stochastic request
- *     whose draft token lies outside [0, V) gets accepted_len -1 and all its
- *     slots -1.  Greedy requests compare such a token like any other id.
- *   - Logits must be finite or -inf, with at least one finite value per row;
- *     NaN / +inf give unspecified (but in-range or -1) results.
+ *     whose draft token lies outside [0, V) gets accepted_len -1, all its
+ *     slots -1 and p_draft, q_draft, resid_mass -1.  Greedy requests compare
+ *     such a token like any other id.
+ *   - Logits must be finite or -inf.  A stochastic request that tests a row
+ *     (target or draft) whose logits are all -inf is reported like one with
+ *     an invalid token; rows after its cut are not looked at.  NaN / +inf
+ *     give unspecified (but in-range or -1) results.
+ *   - Temperature: every kernel uses the one fp32 scale c = fl(log2(e)/T), so
+ *     the distributions are softmax(z / T') with T' = log2(e)/c, within a
+ *     relative 2^-24 of T.
  *   - Unused out_tokens slots (after the committed a_b + 1 tokens) are -1.
  *   - No C++ exception crosses this interface.
  */

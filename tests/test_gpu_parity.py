@@ -110,6 +110,82 @@ def test_extreme_temperatures(T):
     assert near <= 1
 
 
+def test_rows_without_mass_and_huge_scaled_logits():
+    """A stochastic row whose logits are all -inf has no distribution: a request
+    that tests such a row reports -1, a request cut before it is verified
+    normally.  Logits with |z| * log2(e)/T far above FLT_MAX (T = 1e-37, z = 100)
+    are verified like any others.  All launch plans and early exit agree."""
+    import draft_token_verification_row_amd as sv
+    T = float(np.float32(1e-37))
+    batch = synth.make_batch(3, DEV, B=6, V=1000, k=2, seed=5)
+    assert np.all(batch.num_draft == 2) and np.all(batch.greedy == 0)
+    batch.temperature = T
+    g = torch.Generator(device="cpu").manual_seed(11)
+    tgt = torch.randn(batch.target.shape, generator=g).clamp(-5, 5).to(DEV, batch.target.dtype)
+    drf = torch.randn(batch.draft.shape, generator=g).clamp(-5, 5).to(DEV, batch.draft.dtype)
+    toks = batch.tokens.clone()
+    off = batch.offsets
+    inf = float("inf")
+
+    def trow(b, i):
+        return int(off[b]) + b + i
+
+    def drow(b, i):
+        return int(off[b]) + i
+
+    def accept_at(b, i, y):        # y is the unique maximum of both rows: p = q = 1
+        tgt[trow(b, i), y] = 10.0
+        drf[drow(b, i), y] = 10.0
+        toks[drow(b, i)] = y
+
+    def reject_at(b, i, y):        # y is the draft's maximum, far below the target's: p = 0
+        tgt[trow(b, i), y] = -10.0
+        drf[drow(b, i), y] = 10.0
+        toks[drow(b, i)] = y
+
+    reject_at(0, 0, 17)
+    tgt[trow(0, 1)] = -inf         # beyond the cut: not tested
+    accept_at(1, 0, 21)
+    tgt[trow(1, 1)] = -inf         # tested target row without mass
+    accept_at(2, 0, 22)
+    drf[drow(2, 1)] = -inf         # tested draft row without mass
+    tgt[trow(3, 0)] = -inf
+    accept_at(4, 0, 23)
+    accept_at(4, 1, 24)
+    tgt[trow(4, 2)] = -inf         # the bonus row
+    accept_at(5, 0, 25)
+    tgt[trow(5, 1), 4] = 100.0     # |z| * log2(e)/T ~ 1.4e39
+    drf[drow(5, 1), 9] = 100.0
+    toks[drow(5, 1)] = 9           # p(9) = 0: rejected, the residual is one-hot at 4
+    batch.target, batch.draft, batch.tokens = tgt, drf, toks
+    expect_invalid = [1, 2, 3, 4]
+    results = {}
+    for plan in (1, 2):
+        sv.spec_verify_set_launch_plan(plan)
+        try:
+            results[plan] = run_hip(batch)
+        finally:
+            sv.spec_verify_set_launch_plan(0)
+    results["ee"] = run_hip(batch, max_k=2)
+    good = [0, 5]
+    ref = run_oracle(synth.select_requests(batch, good, device="cpu"))
+    for name, got in results.items():
+        acc = got["accepted_len"]
+        assert acc[expect_invalid].tolist() == [-1] * 4, (name, acc)
+        for b in expect_invalid:
+            assert np.all(got["out_tokens"][trow(b, 0):trow(b, 2) + 1] == -1), (name, b)
+            assert np.all(got["p_draft"][drow(b, 0):drow(b, 1) + 1] == -1), (name, b)
+            assert got["resid_mass"][b] == -1, (name, b)
+        assert acc[good].tolist() == ref["accepted_len"].tolist() == [0, 1], (name, acc)
+        for j, b in enumerate(good):
+            sl = slice(trow(b, 0), trow(b, 2) + 1)
+            assert got["out_tokens"][sl].tolist() == ref["out_tokens"][3 * j:3 * j + 3].tolist(), (name, b)
+        assert got["out_tokens"][trow(5, 1)] == 4
+    for k in ("accepted_len", "out_tokens", "resid_mass"):
+        assert np.array_equal(results[1][k], results[2][k]), k
+        assert np.array_equal(results[1][k], results["ee"][k]), k
+
+
 def test_masked_vocabulary_columns():
     batch = synth.make_batch(5, DEV, B=20, V=40000)
     batch.target[:, -3000:] = float("-inf")
