@@ -85,6 +85,32 @@ class HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def early_exit_windows(max_k: int):
+    """Position windows [lo, hi) of the early-exit rounds the library launches
+    for this max_k: 0, 1, 2, 4, 8, ... up to max_k + 1."""
+    end = int(max_k) + 1
+    out, lo, r = [], 0, 0
+    while lo < end:
+        hi = min(1 << r, end)
+        out.append((lo, hi))
+        lo, r = hi, r + 1
+    return out
+
+
+def early_exit_rows_read(acc, num_draft, stochastic, max_k: int) -> int:
+    """Logit rows an early-exit call streams for row statistics, given its
+    outcome: every row of the windows up to the one that holds each cut."""
+    wins = early_exit_windows(max_k)
+    total = 0
+    for a, k, st in zip(acc, num_draft, stochastic):
+        a, k = int(a), int(k)
+        if a < 0:
+            continue
+        hi = next(h for (lo, h) in wins if lo <= a < h)
+        total += min(hi, k + 1) + (min(hi, k) if st else 0)
+    return total
+
+
 def host_cpu() -> str:
     """CPU model and logical core count of the machine the oracle runs on."""
     model = "unknown CPU"
@@ -445,9 +471,9 @@ def main():
     def rows_read(early_exit: bool) -> int:
         if not early_exit:      # every target row, the draft rows of stochastic requests
             return batch.K + batch.B + int(k_np[stoch].sum())
-        # up to each cut: a_b + 1 target rows, min(a_b + 1, k_b) draft rows
+        # every row of the position windows up to the one holding each cut
         a_np = acc.cpu().numpy().astype(np.int64)
-        return int((a_np + 1).sum() + np.minimum(a_np + 1, k_np)[stoch].sum())
+        return early_exit_rows_read(a_np, k_np, stoch, kmax)
 
     bytes_all = rows_read(False) * batch.V * es
     flush = args.mall_flush == "on" or (args.mall_flush == "auto" and bytes_all < (768 << 20))

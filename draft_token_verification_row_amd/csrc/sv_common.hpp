@@ -43,11 +43,15 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 #endif
 constexpr int kUnroll = SV_UNROLL;       // 16-byte chunks per lane per step of a unit loop
 #ifndef SV_ROUND_UNROLL
-#define SV_ROUND_UNROLL 2
+#define SV_ROUND_UNROLL 4
 #endif
 // early-exit rounds: same per-lane chunk order (so the same partials bit for
 // bit), more loads in flight for the small late rounds
 constexpr int kRoundUnroll = SV_ROUND_UNROLL;
+#ifndef SV_ROUND_RESID_UNROLL
+#define SV_ROUND_RESID_UNROLL 1
+#endif
+constexpr int kRoundResidUnroll = SV_ROUND_RESID_UNROLL;   // residual pairs in the rounds
 #ifndef SV_RESID_UNROLL
 #define SV_RESID_UNROLL 1
 #endif
@@ -101,7 +105,7 @@ struct Workspace {
   Partial* pt;         // [(K + B) * nseg]
   Partial* pd;         // [K * nseg]
   double* rp;          // [B * nrseg]
-  uint32_t* rows_r;    // [3][2B]    early-exit rounds: row descriptors
+  uint32_t* rows_r;    // [3][2K+B]  early-exit rounds: row descriptors
   int* res_r;          // [3][B]     early-exit rounds: requests whose residual is swept
   int* alive;          // [3][B]     early-exit rounds: requests deciding a position
 };
@@ -127,6 +131,7 @@ struct Args {
   const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
   const int* rowcount;       // number of rows in rowlist
   int ee_round;              // early-exit round, -1 on the all-rows path
+  int ee_lo, ee_hi, ee_nhi;  // early exit: positions [lo, hi) decided in this round, [hi, nhi) in the next
   int max_k;                 // early-exit: bound on every num_draft[b] (trees: on every depth)
   const int* parent;         // token trees: [N] local parent index
   int* path;                 // token trees: [N] walked node indices

@@ -316,6 +316,7 @@ int32_t run_tree(const sv_tree_t* tr, int32_t* acc_len, int32_t* path, int32_t* 
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
   a.ee_round = early_exit ? 0 : -1;
+  a.ee_lo = a.ee_hi = a.ee_nhi = 0;
   a.max_k = early_exit ? max_depth : 0;
 
   const bool vec = ((uintptr_t)tr->target % 16 == 0) && ((tr->target_ld * es) % 16 == 0);

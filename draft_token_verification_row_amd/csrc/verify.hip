@@ -29,9 +29,10 @@
 //               the correction / bonus token.
 //
 // Early-exit pipeline (the *_early_exit entry points): k_plan_ee, then per
-// draft position j a k_round launch (row statistics of position j of the
-// requests still undecided, residual sweeps of the requests cut at j - 1) and a
-// k_decide_round launch (decides position j), then k_finalize.
+// window of positions a k_round launch (row statistics of the window's rows
+// of the requests still undecided, residual sweeps of the requests cut in the
+// previous window) and a k_decide_round launch (decides the window), one more
+// k_round for the last window's residual sweeps, then k_finalize.
 //
 // Numerics.  Every exponent is exp2((z - m) * c) with one fp32 scale
 // c = fl(log2(e)/T): all kernels compute the softmax at the temperature
@@ -906,13 +907,19 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
 }
 
 // ------------------------------------------------------------------ early exit
-// Left-to-right verification that reads only the rows up to each request's
-// cut.  Round j is two launches: k_round streams the position-j rows of every
-// request still undecided (and the residual row pairs of the requests cut at
-// j - 1), then k_decide_round decides position j of those requests and lists
-// the kept ones, their next rows and the new residual sweeps for round j + 1.
-// Lists rotate over three buffers; k_round of round j clears the counts of
-// the list that k_decide_round of round j fills.  No kernel waits on another
+// Left-to-right verification that reads the rows only up to a window past each
+// request's cut.  Round r covers the positions [P_r, P_(r+1)) with P = 0, 1,
+// 2, 4, 8, ... (the last window ends at max_k + 1), so a call is about
+// log2(max_k) + 2 rounds instead of one per position; a request cut inside a
+// window has had the rest of that window read for nothing (at most as many
+// rows as it had kept before the window).  Round r is two launches: k_round
+// streams the window's rows of every request still undecided (and the
+// residual row pairs of the requests cut in round r - 1), then k_decide_round
+// decides those positions in order, up to the first rejection, and lists the
+// kept requests with the rows of their next window, and the new residual
+// sweeps.  One more k_round sweeps the residuals of the last window's cuts.
+// Lists rotate over three buffers; k_round of round r clears the counts of
+// the list that k_decide_round of round r fills.  No kernel waits on another
 // wavefront: every hand-over is a kernel boundary.
 
 // One workgroup: offsets as in k_plan, every output set to -1 (slots no round
@@ -986,9 +993,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
       a.ws.req[b] = r;
       a.ws.alive[b] = b;
       const long long trow = off + b;
-      if (roff < 2ll * a.B && trow < (long long)a.K + a.B)
+      if (roff < 2ll * a.K + a.B && trow < (long long)a.K + a.B)
         a.ws.rows_r[roff] = (uint32_t)trow | (g ? kGreedyBit : 0u);
-      if (pair && roff + 1 < 2ll * a.B && off < a.K)
+      if (pair && roff + 1 < 2ll * a.K + a.B && off < a.K)
         a.ws.rows_r[roff + 1] = (uint32_t)off | kDraftBit;
     }
     carry_k += tot_k;
@@ -1011,129 +1018,179 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
   }
 }
 
-// Decision of position j of request b by one wavefront.  Lane 0 combines the
-// target row and lane 1 the draft row with the per-row combines of k_decide,
-// so both paths see the same statistics bit for bit.
+// Decision of the positions [lo, hi) of request b (up to its cut) by one
+// wavefront, 32 positions at a time: lane l < 32 combines the target row of
+// position base + l and lane l + 32 its draft row, with the per-row combines
+// of k_decide, so both paths see the same statistics bit for bit.  A request
+// that keeps every position of the window lists the rows of [hi, nhi) for the
+// next round; a cut lists the request's residual sweep.
 template <class L>
-__device__ __forceinline__ void decide_position(const Args& a, int b, int j, int nxt, int lane) {
+__device__ __forceinline__ void decide_window(const Args& a, int b, int lo, int hi, int nhi,
+                                              int nxt, int lane) {
   Header* hdr = a.ws.hdr;
   const ReqInfo R = a.ws.req[b];
   const int k = R.k;
   const bool g = R.greedy != 0;
-  const int trow = R.off + b + j;
-  const int drow = R.off + j;
+  const int trow0 = R.off + b;
+  const int drow0 = R.off;
   const int nseg = a.nseg;
-  if (j == 0 && !g) {
+  const int half = lane & 31;
+  const bool upper = lane >= 32;
+  if (lo == 0 && !g) {
     // a stochastic request with a draft token outside [0, V) reports -1
     // everywhere, as on the all-rows path: all its tokens are tested up front
     bool bad = false;
     for (int i = lane; i < k; i += kWave) {
-      const int y = a.tokens[R.off + i];
+      const int y = a.tokens[drow0 + i];
       bad |= (y < 0 || y >= a.V);
     }
     if (__any(bad)) return;             // outputs keep the -1 written by the plan
   }
-  // loads that depend only on the request are issued before the row combines
-  int y = 0;
-  float zy = 0.f, dy = 0.f, u = 0.f;
-  if (lane == 0 && j < k) {
-    y = a.tokens[drow];
-    if (!g) {
-      u = a.u_accept[drow];
-      if (y >= 0 && y < a.V) {          // checked for every token in round 0
-        zy = logit_at<L>(a.target, trow, a.tld, y);
-        dy = logit_at<L>(a.draft, drow, a.dld, y);
+  const int end = min(hi, k + 1);       // positions lo .. end - 1 (position k: the final token)
+  const int dend = min(hi, k);          // positions with a draft token
+  int A = -1;                           // cut position, -1 while every position is kept
+  bool bonus = false;                   // position k reached: every draft kept
+  bool no_mass = false;                 // a tested row has no mass: the request is invalid
+  float MpA = 0.f, MqA = 0.f;
+  double SpA = 0.0, SqA = 0.0;
+  int amaxA = INT_MAX;
+  for (int base = lo; base < end && A < 0 && !bonus; base += 32) {
+    const int i = base + half;
+    // loads that depend only on the request are issued before the row combines
+    int y = 0;
+    float zy = 0.f, dy = 0.f, u = 0.f;
+    if (!upper && i < dend) {
+      y = a.tokens[drow0 + i];
+      if (!g) {
+        u = a.u_accept[drow0 + i];
+        if (y >= 0 && y < a.V) {        // checked for every token in the first window
+          zy = logit_at<L>(a.target, trow0 + i, a.tld, y);
+          dy = logit_at<L>(a.draft, drow0 + i, a.dld, y);
+        }
       }
     }
+    float M = 0.f;
+    double S = 0.0;
+    int amax = INT_MAX;
+    if (!upper && i < end) {
+      const Partial* P = a.ws.pt + (int64_t)(trow0 + i) * nseg;
+      if (g)
+        row_argmax(P, nseg, amax);
+      else
+        row_softmax(P, nseg, a.c, M, S);
+    } else if (upper && !g && i < dend) {
+      row_softmax(a.ws.pd + (int64_t)(drow0 + i) * nseg, nseg, a.c, M, S);
+    }
+    const float Mq = __shfl(M, half + 32);
+    const double Sq = __shfl(S, half + 32);
+    const bool own_ok = g || row_has_mass(S);
+    const bool draft_ok = __shfl(own_ok, half + 32);
+    const bool pos_ok = own_ok && (i >= k || draft_ok);    // lanes < 32, positions i < end
+    bool rej = false;
+    double py = 0.0, qy = 0.0;
+    if (!upper && i < dend) {
+      if (g) {
+        rej = (y != amax);
+      } else if (!pos_ok) {
+        rej = true;                     // tested: the request is reported invalid
+      } else {
+        py = exp2(((double)zy - (double)M) * a.c64) / S;
+        qy = exp2(((double)dy - (double)Mq) * a.c64) / Sq;
+        rej = !((double)u * qy < py);
+      }
+    }
+    const unsigned long long rm = __ballot(rej);
+    int last;                           // last position of this chunk that is tested
+    if (rm != 0ull) {
+      A = base + __ffsll((long long)rm) - 1;
+      last = A;
+    } else {
+      last = min(end, base + 32) - 1;
+      if (last == k) bonus = true;
+    }
+    if (__ballot(!upper && i <= last && !pos_ok) != 0ull) {
+      no_mass = true;
+      break;
+    }
+    if (!upper && i <= last && i < k) {
+      if (!g) {
+        if (a.p_out) a.p_out[drow0 + i] = (float)py;
+        if (a.q_out) a.q_out[drow0 + i] = (float)qy;
+      }
+      if (i != A) a.out[trow0 + i] = y;  // kept draft
+    }
+    if (A >= 0 || bonus) {
+      const int src = last - base;
+      MpA = __shfl(M, src);
+      SpA = __shfl(S, src);
+      MqA = __shfl(M, src + 32);
+      SqA = __shfl(S, src + 32);
+      amaxA = __shfl(amax, src);
+    }
   }
-  const bool draft_row = !g && j < k;
-  float M = 0.f;
-  double S = 0.0;
-  int amax = INT_MAX;
-  if (lane == 0 && g) {
-    row_argmax(a.ws.pt + (int64_t)trow * nseg, nseg, amax);
-  } else if (lane == 0 || (lane == 1 && draft_row)) {
-    const Partial* P = (lane == 0) ? a.ws.pt + (int64_t)trow * nseg
-                                   : a.ws.pd + (int64_t)drow * nseg;
-    row_softmax(P, nseg, a.c, M, S);
-  }
-  const float Mq = __shfl(M, 1);
-  const double Sq = __shfl(S, 1);
-  M = __shfl(M, 0);
-  S = __shfl(S, 0);
-  amax = __shfl(amax, 0);
-  if (!g && !(row_has_mass(S) && (j == k || row_has_mass(Sq)))) {
-    // a tested row without mass: the request reports -1 everywhere, as on the
-    // all-rows path (slots and p, q of earlier positions are reset)
-    for (int i = lane; i <= k; i += kWave) a.out[R.off + b + i] = -1;
+  if (no_mass) {
+    // slots, p and q written by earlier windows are reset as well
+    for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
     for (int i = lane; i < k; i += kWave) {
-      if (a.p_out) a.p_out[R.off + i] = -1.f;
-      if (a.q_out) a.q_out[R.off + i] = -1.f;
+      if (a.p_out) a.p_out[drow0 + i] = -1.f;
+      if (a.q_out) a.q_out[drow0 + i] = -1.f;
     }
     if (lane == 0) a.acc_len[b] = -1;
     return;
   }
-  if (j == k) {                         // every draft kept: the final token
+  if (A < 0 && !bonus) {                // every position of the window kept: list [hi, nhi)
+    const int nt = min(nhi, k + 1) - hi;
+    const int nd = g ? 0 : max(0, min(nhi, k) - hi);
+    int ir = 0;
+    if (lane == 0) {
+      const int ia = atomicAdd(&hdr->n_alive3[nxt], 1);
+      a.ws.alive[(int64_t)nxt * a.B + ia] = b;
+      ir = atomicAdd(&hdr->n_rows3[nxt], nt + nd);
+    }
+    ir = __shfl(ir, 0);
+    uint32_t* rows = a.ws.rows_r + (int64_t)nxt * (2ll * a.K + a.B);
+    for (int t = lane; t < nt + nd; t += kWave)
+      rows[ir + t] = (t < nt) ? ((uint32_t)(trow0 + hi + t) | (g ? kGreedyBit : 0u))
+                              : ((uint32_t)(drow0 + hi + (t - nt)) | kDraftBit);
+    return;
+  }
+  if (lane != 0) return;
+  if (bonus) {                          // every draft kept: the final token
+    a.acc_len[b] = k;
     if (g) {
-      if (lane == 0) {
-        a.acc_len[b] = k;
-        a.out[trow] = (amax == INT_MAX) ? -1 : amax;
-      }
-    } else if (lane == 0) {             // drawn by k_finalize after the last round
+      a.out[trow0 + k] = (amaxA == INT_MAX) ? -1 : amaxA;
+    } else {                            // drawn by k_finalize after the last round
       ReqInfo Wr = R;
       Wr.a = k;
-      Wr.trow = trow;
+      Wr.trow = trow0 + k;
       Wr.kind = KIND_BONUS;
-      Wr.Mp = M;
-      Wr.Sp = S;
-      a.acc_len[b] = k;
+      Wr.Mp = MpA;
+      Wr.Sp = SpA;
       a.ws.req[b] = Wr;
     }
     return;
   }
-  if (lane != 0) return;
-  bool rej;
+  a.acc_len[b] = A;                     // cut at A
   if (g) {
-    rej = (y != amax);
-  } else {
-    const double py = exp2(((double)zy - (double)M) * a.c64) / S;
-    const double qy = exp2(((double)dy - (double)Mq) * a.c64) / Sq;
-    rej = !((double)u * qy < py);
-    if (a.p_out) a.p_out[drow] = (float)py;
-    if (a.q_out) a.q_out[drow] = (float)qy;
-  }
-  if (!rej) {                           // keep y_j, list position j + 1
-    a.out[trow] = y;
-    const int ia = atomicAdd(&hdr->n_alive3[nxt], 1);
-    a.ws.alive[(int64_t)nxt * a.B + ia] = b;
-    const bool pair = !g && j + 1 < k;
-    const int ir = atomicAdd(&hdr->n_rows3[nxt], pair ? 2 : 1);
-    uint32_t* rows = a.ws.rows_r + (int64_t)nxt * 2 * a.B;
-    rows[ir] = (uint32_t)(trow + 1) | (g ? kGreedyBit : 0u);
-    if (pair) rows[ir + 1] = (uint32_t)(drow + 1) | kDraftBit;
-  } else {                              // cut at j
-    a.acc_len[b] = j;
-    if (g) {
-      a.out[trow] = (amax == INT_MAX) ? -1 : amax;
-    } else {                            // pair swept in round j + 1, drawn by k_finalize
-      ReqInfo Wr = R;
-      Wr.a = j;
-      Wr.trow = trow;
-      Wr.drow = drow;
-      Wr.y = y;
-      Wr.kind = KIND_RESID;
-      Wr.Mp = M;
-      Wr.Sp = S;
-      Wr.Mq = Mq;
-      Wr.Sq = Sq;
-      a.ws.req[b] = Wr;
-      const int ir = atomicAdd(&hdr->n_res3[nxt], 1);
-      a.ws.res_r[(int64_t)nxt * a.B + ir] = b;
-    }
+    a.out[trow0 + A] = (amaxA == INT_MAX) ? -1 : amaxA;
+  } else {                              // pair swept in the next round, drawn by k_finalize
+    ReqInfo Wr = R;
+    Wr.a = A;
+    Wr.trow = trow0 + A;
+    Wr.drow = drow0 + A;
+    Wr.y = a.tokens[drow0 + A];
+    Wr.kind = KIND_RESID;
+    Wr.Mp = MpA;
+    Wr.Sp = SpA;
+    Wr.Mq = MqA;
+    Wr.Sq = SqA;
+    a.ws.req[b] = Wr;
+    const int ir = atomicAdd(&hdr->n_res3[nxt], 1);
+    a.ws.res_r[(int64_t)nxt * a.B + ir] = b;
   }
 }
 
-// Round j (a.ee_round), streaming half: persistent grid over the round's
+// Round r (a.ee_round), streaming half: persistent grid over the round's
 // units, row units first, then residual units.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_round(Args a) {
@@ -1145,14 +1202,14 @@ __global__ __launch_bounds__(kBlock) void k_round(Args a) {
   const int cur = j % 3, nxt = (j + 1) % 3;
   Header* hdr = a.ws.hdr;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    // the lists k_decide_round of this round fills; round j - 2 read them
+    // the lists k_decide_round of this round fills; round r - 2 read them
     hdr->n_rows3[nxt] = 0;
     hdr->n_res3[nxt] = 0;
     hdr->n_alive3[nxt] = 0;
   }
   const int n_s = hdr->n_rows3[cur] * a.nseg;
   const int n_units = n_s + hdr->n_res3[cur] * a.nrseg;
-  const uint32_t* rows = a.ws.rows_r + (int64_t)cur * 2 * a.B;
+  const uint32_t* rows = a.ws.rows_r + (int64_t)cur * (2ll * a.K + a.B);
   const int* res = a.ws.res_r + (int64_t)cur * a.B;
   const Elem* tgt = static_cast<const Elem*>(a.target);
   const Elem* drf = static_cast<const Elem*>(a.draft);
@@ -1171,7 +1228,7 @@ __global__ __launch_bounds__(kBlock) void k_round(Args a) {
         argmax_unit<L, kRoundUnroll>(base, s0, s1, lane, out);
       else
         softmax_unit<L, kRoundUnroll>(base, s0, s1, lane, a, out);
-    } else {                            // residual unit of a request cut at j - 1
+    } else {                            // residual unit of a request cut in round r - 1
       const int v = u - n_s;
       const int ri = v / a.nrseg;
       const int seg = v - ri * a.nrseg;
@@ -1181,13 +1238,13 @@ __global__ __launch_bounds__(kBlock) void k_round(Args a) {
       const Elem* dp = drf + (int64_t)R.drow * a.dld;
       const int s0 = seg * a.rseg;
       const int s1 = min(s0 + a.rseg, a.V);
-      const double tot = resid_unit<L, kRoundUnroll>(tp, dp, resid_weights(R, a), R.y, s0, s1, lane);
+      const double tot = resid_unit<L, kRoundResidUnroll>(tp, dp, resid_weights(R, a), R.y, s0, s1, lane);
       if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
     }
   }
 }
 
-// Round j, deciding half: one wavefront per request whose position-j rows the
+// Round r, deciding half: one wavefront per request whose window rows the
 // round streamed.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_decide_round(Args a) {
@@ -1198,7 +1255,7 @@ __global__ __launch_bounds__(kBlock) void k_decide_round(Args a) {
   const int cur = j % 3, nxt = (j + 1) % 3;
   const int nal = a.ws.hdr->n_alive3[cur];
   for (int w = gw; w < nal; w += W)
-    decide_position<L>(a, a.ws.alive[(int64_t)cur * a.B + w], j, nxt, lane);
+    decide_window<L>(a, a.ws.alive[(int64_t)cur * a.B + w], a.ee_lo, a.ee_hi, a.ee_nhi, nxt, lane);
 }
 
 // ------------------------------------------------------------------ host side
@@ -1224,7 +1281,7 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)((K + B) * nseg), 256);
   z->off_pd = o; o = align_up(o + sizeof(Partial) * (size_t)(K * nseg), 256);
   z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nrseg), 256);
-  z->off_rows_r = o; o = align_up(o + 4 * (size_t)(6 * B), 256);
+  z->off_rows_r = o; o = align_up(o + 4 * (size_t)(3 * (2 * K + B)), 256);
   z->off_res_r = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
   z->off_alive = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
   z->total = o + 256;   // slack for aligning the caller's pointer
@@ -1275,17 +1332,34 @@ template <class L>
 void launch_early_exit(const Args& a, hipStream_t st, int dev, bool sample) {
   static std::atomic<int> occ_round[64];
   const long long cus = cu_count(dev);
-  const long long units_max = 2ll * a.B * a.nseg + (long long)a.B * a.nrseg;
+  const long long units_max = (2ll * a.K + a.B) * a.nseg + (long long)a.B * a.nrseg;
   const long long cap = cus * resident_blocks(occ_round, k_round<L>, dev);
   const int grid = (int)std::max(1ll, std::min(cap, (units_max + kWavesPerBlock - 1) / kWavesPerBlock));
   const int grid_dec = (int)std::max(1ll, std::min(cus * kBlocksPerCU, ((long long)a.B + kWavesPerBlock - 1) / kWavesPerBlock));
   k_plan_ee<<<1, kPlanThreads, 0, st>>>(a);
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
-  for (int j = 0; j <= a.max_k; ++j) {
-    Args r = a;
-    r.ee_round = j;
-    k_round<L><<<grid, kBlock, 0, st>>>(r);
-    k_decide_round<L><<<grid_dec, kBlock, 0, st>>>(r);
+  // windows [P_r, P_(r+1)) with P = 0, 1, 2, 4, 8, ..., the last one ending at
+  // max_k + 1; k_plan_ee lists the rows of the first window (position 0)
+  const int end = a.max_k + 1;
+  auto start = [](int r) { return r == 0 ? 0 : (1 << (r - 1)); };
+  int r = 0;
+  int lo = 0;
+  while (lo < end) {
+    const int hi = std::min(start(r + 1), end);
+    Args ra = a;
+    ra.ee_round = r;
+    ra.ee_lo = lo;
+    ra.ee_hi = hi;
+    ra.ee_nhi = std::min(start(r + 2), end);
+    k_round<L><<<grid, kBlock, 0, st>>>(ra);
+    k_decide_round<L><<<grid_dec, kBlock, 0, st>>>(ra);
+    if (hi >= end && lo < end - 1) {
+      // residual sweeps of the cuts in the last window (no rows are listed)
+      ra.ee_round = r + 1;
+      k_round<L><<<grid, kBlock, 0, st>>>(ra);
+    }
+    lo = hi;
+    ++r;
   }
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
   if (sample) k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
@@ -1365,6 +1439,7 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
   a.ee_round = -1;
+  a.ee_lo = a.ee_hi = a.ee_nhi = 0;
   a.max_k = max_k;
 
   bool vec = ((uintptr_t)bt->target % 16 == 0) && ((bt->target_ld * es) % 16 == 0);

@@ -138,12 +138,15 @@ int32_t spec_verify_sample(const sv_batch_t* batch, float temperature,
  * blog, "Core idea of speculative decoding": drafts after the first rejection
  * are discarded, so their rows need not be read).  Same results as
  * spec_verify_greedy / spec_verify_sample for accepted_len, out_tokens and
- * resid_mass, bit for bit, but reads only the rows up to each request's cut:
- * position j of every request still alive is verified in round j, one round
- * per two kernel launches.
+ * resid_mass, bit for bit, but reads the rows only up to a window past each
+ * request's cut.  Round r verifies the positions [P_r, P_(r+1)) of every
+ * request still alive, with P = 0, 1, 2, 4, 8, ... and the last window ending
+ * at max_k + 1 (two kernel launches per round, plus one launch for the
+ * residual sweeps of the last window's cuts); a request cut inside a window
+ * has the rest of that window read but not used.
  *   max_k     bound on every num_draft[b], 0 <= max_k <= 4096; the call runs
- *             max_k + 1 rounds.  A request with num_draft[b] > max_k is a
- *             device-side input error (every output -1, as for an
+ *             about log2(max_k) + 2 rounds.  A request with num_draft[b] >
+ *             max_k is a device-side input error (every output -1, as for an
  *             inconsistent num_draft).
  *   p_draft, q_draft  p(y_i), q(y_i) of the positions actually tested (every
  *             position up to and including the cut); -1 for later positions,
