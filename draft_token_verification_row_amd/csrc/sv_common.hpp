@@ -86,6 +86,10 @@ struct ReqInfo {      // per request; plan fills off/k/greedy, decide the rest
   double Sp, Sq;
 };
 
+struct __align__(16) AliveEntry {   // early exit: a request still deciding, with
+  int b, off, k, greedy;            // what its decision needs, in one 16-byte load
+};
+
 struct Header {
   int error;
   int n_rows;
@@ -107,7 +111,8 @@ struct Workspace {
   double* rp;          // [B * nrseg]
   uint32_t* rows_r;    // [3][2K+B]  early-exit rounds: row descriptors
   int* res_r;          // [3][B]     early-exit rounds: requests whose residual is swept
-  int* alive;          // [3][B]     early-exit rounds: requests deciding a position
+  int* alive;          // [3][B]     tree rounds: requests still walking
+  AliveEntry* alive_e; // [3][B]     early-exit rounds: requests deciding a window
 };
 
 struct Args {

@@ -313,6 +313,7 @@ int32_t run_tree(const sv_tree_t* tr, int32_t* acc_len, int32_t* path, int32_t* 
   a.ws.rowdesc = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc);
   a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
   a.ws.alive = reinterpret_cast<int*>(wb + z.off_alive);
+  a.ws.alive_e = nullptr;
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
   a.ee_round = early_exit ? 0 : -1;

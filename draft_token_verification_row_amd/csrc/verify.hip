@@ -991,7 +991,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
       r.pad0 = r.pad1 = 0;
       r.Sp = r.Sq = 0.0;
       a.ws.req[b] = r;
-      a.ws.alive[b] = b;
+      AliveEntry e;
+      e.b = b;
+      e.off = (int)off;
+      e.k = (int)k;
+      e.greedy = g;
+      a.ws.alive_e[b] = e;
       const long long trow = off + b;
       if (roff < 2ll * a.K + a.B && trow < (long long)a.K + a.B)
         a.ws.rows_r[roff] = (uint32_t)trow | (g ? kGreedyBit : 0u);
@@ -1025,14 +1030,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
 // that keeps every position of the window lists the rows of [hi, nhi) for the
 // next round; a cut lists the request's residual sweep.
 template <class L>
-__device__ __forceinline__ void decide_window(const Args& a, int b, int lo, int hi, int nhi,
-                                              int nxt, int lane) {
+__device__ __forceinline__ void decide_window(const Args& a, const AliveEntry& e, int lo, int hi,
+                                              int nhi, int nxt, int lane) {
   Header* hdr = a.ws.hdr;
-  const ReqInfo R = a.ws.req[b];
-  const int k = R.k;
-  const bool g = R.greedy != 0;
-  const int trow0 = R.off + b;
-  const int drow0 = R.off;
+  const int b = e.b;
+  const int k = e.k;
+  const bool g = e.greedy != 0;
+  const int trow0 = e.off + b;
+  const int drow0 = e.off;
   const int nseg = a.nseg;
   const int half = lane & 31;
   const bool upper = lane >= 32;
@@ -1144,7 +1149,7 @@ __device__ __forceinline__ void decide_window(const Args& a, int b, int lo, int 
     int ir = 0;
     if (lane == 0) {
       const int ia = atomicAdd(&hdr->n_alive3[nxt], 1);
-      a.ws.alive[(int64_t)nxt * a.B + ia] = b;
+      a.ws.alive_e[(int64_t)nxt * a.B + ia] = e;
       ir = atomicAdd(&hdr->n_rows3[nxt], nt + nd);
     }
     ir = __shfl(ir, 0);
@@ -1155,12 +1160,21 @@ __device__ __forceinline__ void decide_window(const Args& a, int b, int lo, int 
     return;
   }
   if (lane != 0) return;
+  ReqInfo Wr;                           // the record k_round and k_finalize read
+  Wr.off = e.off;
+  Wr.k = k;
+  Wr.greedy = e.greedy;
+  Wr.pad0 = Wr.pad1 = 0;
+  Wr.Mq = 0.f;
+  Wr.Sq = 0.0;
+  Wr.y = -1;
+  Wr.drow = -1;
+  Wr.kind = KIND_NONE;
   if (bonus) {                          // every draft kept: the final token
     a.acc_len[b] = k;
     if (g) {
       a.out[trow0 + k] = (amaxA == INT_MAX) ? -1 : amaxA;
     } else {                            // drawn by k_finalize after the last round
-      ReqInfo Wr = R;
       Wr.a = k;
       Wr.trow = trow0 + k;
       Wr.kind = KIND_BONUS;
@@ -1174,7 +1188,6 @@ __device__ __forceinline__ void decide_window(const Args& a, int b, int lo, int 
   if (g) {
     a.out[trow0 + A] = (amaxA == INT_MAX) ? -1 : amaxA;
   } else {                              // pair swept in the next round, drawn by k_finalize
-    ReqInfo Wr = R;
     Wr.a = A;
     Wr.trow = trow0 + A;
     Wr.drow = drow0 + A;
@@ -1253,9 +1266,16 @@ __global__ __launch_bounds__(kBlock) void k_decide_round(Args a) {
   const int W = gridDim.x * kWavesPerBlock;
   const int j = a.ee_round;
   const int cur = j % 3, nxt = (j + 1) % 3;
+  const AliveEntry* list = a.ws.alive_e + (int64_t)cur * a.B;
+  // the first entry is loaded together with the count (every index < B is in
+  // the buffer; entries at or past the count are not used)
+  AliveEntry e;
+  if (gw < a.B) e = list[gw];
   const int nal = a.ws.hdr->n_alive3[cur];
-  for (int w = gw; w < nal; w += W)
-    decide_window<L>(a, a.ws.alive[(int64_t)cur * a.B + w], a.ee_lo, a.ee_hi, a.ee_nhi, nxt, lane);
+  for (int w = gw; w < nal; w += W) {
+    if (w != gw) e = list[w];
+    decide_window<L>(a, e, a.ee_lo, a.ee_hi, a.ee_nhi, nxt, lane);
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -1283,7 +1303,7 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   z->off_rp = o; o = align_up(o + sizeof(double) * (size_t)(B * nrseg), 256);
   z->off_rows_r = o; o = align_up(o + 4 * (size_t)(3 * (2 * K + B)), 256);
   z->off_res_r = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
-  z->off_alive = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
+  z->off_alive = o; o = align_up(o + sizeof(AliveEntry) * (size_t)(3 * B), 256);
   z->total = o + 256;   // slack for aligning the caller's pointer
   return true;
 }
@@ -1435,7 +1455,8 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.ws.rp = reinterpret_cast<double*>(wb + z.off_rp);
   a.ws.rows_r = reinterpret_cast<uint32_t*>(wb + z.off_rows_r);
   a.ws.res_r = reinterpret_cast<int*>(wb + z.off_res_r);
-  a.ws.alive = reinterpret_cast<int*>(wb + z.off_alive);
+  a.ws.alive = nullptr;
+  a.ws.alive_e = reinterpret_cast<AliveEntry*>(wb + z.off_alive);
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
   a.ee_round = -1;

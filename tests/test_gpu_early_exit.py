@@ -179,3 +179,50 @@ def test_early_exit_full_size(cfg):
     near = compare(sub, sel, _oracle_as_tested(sub, sel, ref), f"early-exit full cfg{cfg}")
     _log(f"[early-exit full] cfg={cfg}: sampled {len(reqs)}, near_ties={near}")
     assert near <= 1
+
+
+@pytest.mark.parametrize("extra", [0, 70])
+def test_early_exit_long_runs_span_wide_windows(extra):
+    """Requests that keep long runs of drafts reach the late windows, up to 64
+    positions wide (two 32-position chunks of the deciding wavefront): p = q on
+    every stochastic position (kept for any u < 1), greedy drafts equal to the
+    target argmax, and one forced cut per kind of request deep in a window."""
+    rng = np.random.default_rng(123)
+    V = 257
+    ks = [0, 1, 31, 32, 33, 64, 100, 130, 70, 45]
+    greedy = [0, 1, 0, 1, 0, 1, 0, 1, 0, 1]
+    cut = {8: 69, 9: 40}
+    B, K = len(ks), sum(ks)
+    off = np.concatenate([[0], np.cumsum(ks)])
+    tgt = torch.as_tensor(rng.normal(0, 2, size=(K + B, V)).astype(np.float32))
+    tgt = tgt.to(torch.bfloat16).to(torch.float32).numpy()       # values bf16 holds exactly
+    drf = np.zeros((K, V), np.float32)
+    toks = np.zeros(K, np.int64)
+    for b in range(B):
+        for i in range(ks[b]):
+            t = tgt[off[b] + b + i]
+            d = t.copy()
+            if greedy[b]:
+                y = int(np.argmax(t))
+                if cut.get(b) == i:
+                    y = (y + 1) % V
+            else:
+                y = int(rng.integers(V))
+                if cut.get(b) == i:
+                    y = int(np.argmin(t))
+                    d[y] = float(t.max()) + 8.0      # q(y) ~ 1, p(y) tiny: rejected
+            drf[off[b] + i] = d
+            toks[off[b] + i] = y
+    u = (rng.random(K) * 0.9 + 0.05).astype(np.float32)
+    uf = rng.random(B).astype(np.float32)
+    batch = synth.from_arrays(tgt, drf, toks, ks, greedy=greedy, temperature=1.0, u_accept=u,
+                              u_final=uf, dtype="bf16", name="long_runs", device=DEV)
+    max_k = max(ks) + extra
+    _log(f"[early-exit] long runs, max_k={max_k}")
+    got = run_hip(batch, max_k=max_k)
+    full = run_hip(batch)
+    _assert_same_as_all_rows(batch, got, full, "long runs")
+    want = [cut.get(b, ks[b]) for b in range(B)]
+    assert got["accepted_len"].tolist() == want, got["accepted_len"]
+    ref = run_oracle(batch)
+    compare(batch, got, _oracle_as_tested(batch, got, ref), "long runs")
