@@ -36,12 +36,16 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 #ifndef SV_UNROLL
-#define SV_UNROLL 1
+#define SV_UNROLL 2
 #endif
 #ifndef SV_SEG_BYTES
 #define SV_SEG_BYTES 32768
 #endif
 constexpr int kUnroll = SV_UNROLL;       // 16-byte chunks per lane per step of a unit loop
+#ifndef SV_ARGMAX_UNROLL
+#define SV_ARGMAX_UNROLL 4
+#endif
+constexpr int kArgmaxUnroll = SV_ARGMAX_UNROLL;   // the same for argmax units (less work per chunk)
 #ifndef SV_ROUND_UNROLL
 #define SV_ROUND_UNROLL 4
 #endif
@@ -347,7 +351,7 @@ __device__ void softmax_unit(const typename L::Elem* row, int s0, int s1, int la
   }
 }
 
-template <class L, int U = kUnroll>
+template <class L, int U = kArgmaxUnroll>
 __device__ void argmax_unit(const typename L::Elem* row, int s0, int s1, int lane,
                             Partial* out) {
   ArgmaxAcc<L::E> acc;

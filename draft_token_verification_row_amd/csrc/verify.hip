@@ -553,11 +553,13 @@ struct UnitMass {
 
 // Wave 0 finds the unit holding the crossing of w * Z.  Returns (in lane 0's
 // view, broadcast) the unit, the cumulative mass before it and a fallback flag.
+// m0_pre: the masses of units 0..63 already loaded by the caller (0 past nunits).
 __device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, double& Z,
-                          int& unit, double& before, int& fallback) {
+                          int& unit, double& before, int& fallback,
+                          const double* m0_pre = nullptr) {
   // Z is the total of the same chunked scan that locates the crossing, so the
   // two agree bit for bit; with <= 64 units (the usual case) masses load once.
-  double m0 = (lane < nunits) ? um(lane) : 0.0;
+  double m0 = m0_pre ? *m0_pre : ((lane < nunits) ? um(lane) : 0.0);
   double tot = 0.0;
   for (int c0 = 0; c0 < nunits; c0 += kWave) {
     const double m = (c0 == 0) ? m0 : ((c0 + lane < nunits) ? um(c0 + lane) : 0.0);
@@ -719,16 +721,18 @@ struct FinalizeShared {
 
 // Correction or bonus draw of request b by one block of >= kBlock threads
 // (KEEP: see rescan_unit).
+// The request record R, the uniform w and (wave 0, lane l) the residual mass
+// of unit l (rp_pre; 0 past nrseg) are loaded by the caller, so that they can
+// be requested together.
 template <class L, bool KEEP>
-__device__ __forceinline__ void finalize_request(const Args& a, int b, FinalizeShared& sh) {
+__device__ __forceinline__ void finalize_request(const Args& a, int b, const ReqInfo& R, double w,
+                                                 double rp_pre, FinalizeShared& sh) {
   using Elem = typename L::Elem;
   constexpr int PER_S = kSegBytes / (int)sizeof(Elem) / kBlock;    // k_stats unit
   constexpr int PER_R = kRSegBytes / (int)sizeof(Elem) / kBlock;   // k_resid unit
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const ReqInfo R = a.ws.req[b];
   if (R.kind != KIND_RESID && R.kind != KIND_BONUS) return;
-  const double w = (double)a.u_final[b];
   if (tid < kWave) {
     UnitMass um;
     um.rp = a.ws.rp + (int64_t)b * a.nrseg;
@@ -740,7 +744,8 @@ __device__ __forceinline__ void finalize_request(const Args& a, int b, FinalizeS
     int mode = um.resid ? DRAW_RESID : DRAW_FROM_P;
     double Z = 0.0, before = 0.0;
     int unit = 0, fb = 0;
-    find_unit(um, um.resid ? a.nrseg : a.nseg, w, lane, Z, unit, before, fb);
+    find_unit(um, um.resid ? a.nrseg : a.nseg, w, lane, Z, unit, before, fb,
+              (um.resid && a.nrseg <= kWave) ? &rp_pre : nullptr);
     if (mode == DRAW_RESID && !(Z > 0.0)) {     // p == q numerically: draw from p
       mode = DRAW_FROM_P;
       um.resid = false;
@@ -779,11 +784,29 @@ __device__ __forceinline__ void finalize_request(const Args& a, int b, FinalizeS
   }
 }
 
+// Loads of a draw that depend only on the request index, issued together
+// (the residual masses are read whether or not the request has a residual;
+// they lie in the workspace either way and are used only for a residual draw).
+struct DrawInputs {
+  ReqInfo R;
+  double w, rp;
+};
+
+__device__ __forceinline__ DrawInputs draw_inputs(const Args& a, int b) {
+  DrawInputs d;
+  const int lane = threadIdx.x & (kWave - 1);
+  d.rp = (threadIdx.x < kWave && lane < a.nrseg) ? a.ws.rp[(int64_t)b * a.nrseg + lane] : 0.0;
+  d.R = a.ws.req[b];
+  d.w = (double)a.u_final[b];
+  return d;
+}
+
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
   __shared__ FinalizeShared sh;
+  const DrawInputs d = draw_inputs(a, blockIdx.x);
   if (a.ws.hdr->error) return;
-  finalize_request<L, true>(a, blockIdx.x, sh);
+  finalize_request<L, true>(a, blockIdx.x, d.R, d.w, d.rp, sh);
 }
 
 // ------------------------------------------------------------------ single-launch path
@@ -903,7 +926,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
     }
     __syncthreads();
   }
-  finalize_request<L, false>(a, b, sh);
+  const DrawInputs d = draw_inputs(a, b);
+  finalize_request<L, false>(a, b, d.R, d.w, d.rp, sh);
 }
 
 // ------------------------------------------------------------------ early exit
