@@ -229,7 +229,27 @@ def bench_tree(args, sv, torch):
     def rows_read(early_exit):
         if not early_exit:
             return tb.N
-        return int((acc.cpu().numpy().astype(np.int64) + 1).sum())
+        # per round: each walk's current node and its descendants down to the
+        # window's last step (the rows the round streams)
+        a_np = acc.cpu().numpy().astype(np.int64)
+        p_np = path.cpu().numpy().astype(np.int64)
+        total = 0
+        for b in range(tb.B):
+            o, n = int(off[b]), int(tb.num_nodes[b])
+            for lo, hi in early_exit_windows(depth):
+                if a_np[b] < 0 or lo > a_np[b]:
+                    break
+                c = int(p_np[o + lo])
+                cnt = 1
+                for i in range(c + 1, n):
+                    q = i
+                    for _ in range(hi - lo - 1):
+                        q = int(par[o + q])
+                        if q <= c:
+                            cnt += q == c
+                            break
+                total += cnt
+        return total
 
     step_s, t_k = timed(calls[ee], args.steps)
     bytes_k = rows_read(ee) * tb.V * es

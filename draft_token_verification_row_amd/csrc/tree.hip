@@ -65,7 +65,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_tree_plan(Args a) {
       r.Mp = r.Mq = 0.f;
       r.pad0 = r.pad1 = 0;
       r.Sp = r.Sq = 0.0;
-      if (rounds && n >= 1) a.ws.alive[atomicAdd(&s_na, 1)] = b;   // round 0: at the root
+      if (rounds && n >= 1) {           // round 0: at the root, whose row the round reads
+        const int ia = atomicAdd(&s_na, 1);
+        a.ws.alive[ia] = b;
+        a.ws.rows_r[ia] = (uint32_t)off;
+      }
       a.ws.req[b] = r;
     }
     carry += tot;
@@ -79,7 +83,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_tree_plan(Args a) {
     h->n_units = 0;
     h->n_resid = 0;
     h->n_alive3[0] = (rounds && !bad) ? s_na : 0;   // (list order is free)
+    h->n_rows3[0] = (rounds && !bad) ? s_na : 0;
     h->n_alive3[1] = 0;
+    h->n_rows3[1] = 0;
   }
 }
 
@@ -160,11 +166,15 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(Args a) {
   }
 }
 
-// Early-exit rounds: round j streams the row of the current node of every
-// request still walking (argmax units of kTreeSegBytes, partials kept per
-// request: a round reads at most B rows, so small units keep every CU busy),
-// then one wavefront per such request takes one step.  Lists of walking
-// requests rotate over three buffers.
+// Early-exit rounds.  Round r covers the walk's steps [P_r, P_(r+1)) with
+// P = 0, 1, 2, 4, 8, ... (the last window ends at max_depth + 1): k_tree_round
+// streams the rows listed for the round (argmax units of kTreeSegBytes, so
+// that the few rows of a round still spread over every CU; partials per node
+// row), then one wavefront per walking request takes the window's steps and,
+// if it is still walking, lists its new current node and the descendants the
+// next window can reach.  Lists of rows and of walking requests rotate over
+// three buffers; k_tree_round of round r clears the counts k_tree_step_round
+// of round r fills.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_tree_round(Args a) {
   using Elem = typename L::Elem;
@@ -174,20 +184,61 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(Args a) {
   const int j = a.ee_round;
   const int cur = j % 3, nxt = (j + 1) % 3;
   Header* hdr = a.ws.hdr;
-  if (blockIdx.x == 0 && threadIdx.x == 0) hdr->n_alive3[nxt] = 0;
-  const int n_units = hdr->n_alive3[cur] * a.nseg;
-  const int* alive = a.ws.alive + (int64_t)cur * a.B;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr->n_alive3[nxt] = 0;
+    hdr->n_rows3[nxt] = 0;
+  }
+  const int n_units = hdr->n_rows3[cur] * a.nseg;
+  const uint32_t* rows = a.ws.rows_r + (int64_t)cur * a.K;
   const Elem* tgt = static_cast<const Elem*>(a.target);
   for (int u = gw; u < n_units; u += W) {
-    const int w = u / a.nseg;
-    const int seg = u - w * a.nseg;
-    const int b = alive[w];
-    const int row = a.ws.req[b].trow;
+    const int ri = u / a.nseg;
+    const int seg = u - ri * a.nseg;
+    const int row = (int)rows[ri];
     const int s0 = seg * a.seg;
     const int s1 = min(s0 + a.seg, a.V);
     argmax_unit<L>(tgt + (int64_t)row * a.tld, s0, s1, lane,
-                   a.ws.pt + (int64_t)b * a.nseg + seg);
+                   a.ws.pt + (int64_t)row * a.nseg + seg);
   }
+}
+
+// Node i (local, i > c) lies at most depth levels below node c: its parent
+// chain reaches c within depth links (parents have lower indices, so the
+// chain can stop as soon as it drops below c).
+__device__ __forceinline__ bool tree_below(const Args& a, int off, int c, int i, int depth) {
+  int p = i;
+  for (int s = 0; s < depth; ++s) {
+    p = a.parent[off + p];
+    if (p == c) return true;
+    if (p < c) return false;
+  }
+  return false;
+}
+
+// List node c of request R and its descendants up to depth levels below it
+// (the rows a window of depth + 1 steps from c can visit) for the next round.
+__device__ void tree_list_rows(const Args& a, const ReqInfo& R, int c, int depth, int nxt,
+                               int lane) {
+  int cnt = 1;
+  if (depth > 0)
+    for (int i0 = c + 1; i0 < R.k; i0 += kWave) {
+      const int i = i0 + lane;
+      cnt += __popcll(__ballot(i < R.k && tree_below(a, R.off, c, i, depth)));
+    }
+  int ir = 0;
+  if (lane == 0) ir = atomicAdd(&a.ws.hdr->n_rows3[nxt], cnt);
+  ir = __shfl(ir, 0);
+  uint32_t* rows = a.ws.rows_r + (int64_t)nxt * a.K;
+  if (lane == 0) rows[ir] = (uint32_t)(R.off + c);
+  int pos = ir + 1;
+  if (depth > 0)
+    for (int i0 = c + 1; i0 < R.k; i0 += kWave) {
+      const int i = i0 + lane;
+      const bool d = i < R.k && tree_below(a, R.off, c, i, depth);
+      const unsigned long long m = __ballot(d);
+      if (d) rows[pos + __popcll(m & ((1ull << lane) - 1ull))] = (uint32_t)(R.off + i);
+      pos += __popcll(m);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_tree_step_round(Args a) {
@@ -201,29 +252,37 @@ __global__ __launch_bounds__(kBlock) void k_tree_step_round(Args a) {
   for (int w = gw; w < nal; w += W) {
     const int b = a.ws.alive[(int64_t)cur * a.B + w];
     ReqInfo R = a.ws.req[b];
-    if (j == 0 && !tree_parents_ok(a, R, lane)) continue;   // outputs keep -1
-    const int f = tree_step(a, b, R, a.ws.pt + (int64_t)b * a.nseg, j, lane);
-    if (f < 0) continue;
-    if (j == a.max_k) {
-      // the walk would accept more than max_depth nodes: an input error, the
-      // request reports -1 everywhere
-      for (int i = lane; i <= j; i += kWave) {
-        a.path[R.off + i] = -1;
-        a.out[R.off + i] = -1;
+    if (a.ee_lo == 0 && !tree_parents_ok(a, R, lane)) continue;   // outputs keep -1
+    bool walking = true;
+    for (int t = a.ee_lo; t < a.ee_hi && walking; ++t) {
+      const int f = tree_step(a, b, R, a.ws.pt + (int64_t)R.trow * a.nseg, t, lane);
+      if (f < 0) {
+        walking = false;                // acc_len written by tree_step
+      } else if (t == a.max_k) {
+        // the walk would accept more than max_depth nodes: an input error, the
+        // request reports -1 everywhere
+        for (int i = lane; i <= t; i += kWave) {
+          a.path[R.off + i] = -1;
+          a.out[R.off + i] = -1;
+        }
+        walking = false;
+      } else {
+        R.trow = R.off + f;
       }
-      continue;
     }
+    if (!walking) continue;
     if (lane == 0) {
-      a.ws.req[b].trow = R.off + f;
+      a.ws.req[b].trow = R.trow;
       const int ia = atomicAdd(&hdr->n_alive3[nxt], 1);
       a.ws.alive[(int64_t)nxt * a.B + ia] = b;
     }
+    tree_list_rows(a, R, R.trow - R.off, a.ee_nhi - a.ee_hi - 1, nxt, lane);
   }
 }
 
 // ------------------------------------------------------------------ token trees (host)
 struct TreeSizes {
-  size_t off_hdr, off_req, off_rowdesc, off_pt, off_alive, total;
+  size_t off_hdr, off_req, off_rowdesc, off_pt, off_alive, off_rows_r, total;
 };
 
 bool compute_tree_sizes(long long B, long long N, long long V, TreeSizes* z) {
@@ -231,14 +290,15 @@ bool compute_tree_sizes(long long B, long long N, long long V, TreeSizes* z) {
   if (N >= (1ll << 29)) return false;
   const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
   const long long ntseg = (V + kTreeSegBytes / 4 - 1) / (kTreeSegBytes / 4);
-  if (N * nseg >= (1ll << 31) || B * ntseg >= (1ll << 31)) return false;
-  const long long npart = std::max(N * nseg, B * ntseg);   // all rows, or per-request rounds
+  if (N * ntseg >= (1ll << 31)) return false;
+  const long long npart = N * ntseg;   // every node row, in 32 KiB (all rows) or 4 KiB units
   size_t o = 0;
   z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
   z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);
   z->off_rowdesc = o; o = align_up(o + 4 * (size_t)N, 256);
   z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)npart, 256);
   z->off_alive = o; o = align_up(o + 4 * (size_t)(3 * B), 256);
+  z->off_rows_r = o; o = align_up(o + 4 * (size_t)(3 * N), 256);
   z->total = o + 256;
   return true;
 }
@@ -260,15 +320,23 @@ void launch_tree(const Args& a, hipStream_t st, int dev, bool early_exit) {
     k_tree_walk<<<grid_walk, kBlock, 0, st>>>(a);
     return;
   }
-  const long long units = (long long)a.B * a.nseg;
+  const long long units = (long long)a.K * a.nseg;
   const long long cap = cus * resident_blocks(occ_round, k_tree_round<L>, dev);
   const int grid = (int)std::max(1ll, std::min(cap, (units + kWavesPerBlock - 1) / kWavesPerBlock));
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
-  for (int j = 0; j <= a.max_k; ++j) {
-    Args r = a;
-    r.ee_round = j;
-    k_tree_round<L><<<grid, kBlock, 0, st>>>(r);
-    k_tree_step_round<<<grid_walk, kBlock, 0, st>>>(r);
+  // windows of steps [P_r, P_(r+1)), P = 0, 1, 2, 4, 8, ..., up to max_depth + 1
+  const int end = a.max_k + 1;
+  auto start = [](int r) { return r == 0 ? 0 : (1 << (r - 1)); };
+  for (int r = 0, lo = 0; lo < end; ++r) {
+    const int hi = std::min(start(r + 1), end);
+    Args ra = a;
+    ra.ee_round = r;
+    ra.ee_lo = lo;
+    ra.ee_hi = hi;
+    ra.ee_nhi = std::min(start(r + 2), end);
+    k_tree_round<L><<<grid, kBlock, 0, st>>>(ra);
+    k_tree_step_round<<<grid_walk, kBlock, 0, st>>>(ra);
+    lo = hi;
   }
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
 }
@@ -314,6 +382,7 @@ int32_t run_tree(const sv_tree_t* tr, int32_t* acc_len, int32_t* path, int32_t* 
   a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
   a.ws.alive = reinterpret_cast<int*>(wb + z.off_alive);
   a.ws.alive_e = nullptr;
+  a.ws.rows_r = reinterpret_cast<uint32_t*>(wb + z.off_rows_r);
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
   a.ee_round = early_exit ? 0 : -1;

@@ -228,11 +228,14 @@ int32_t spec_verify_tree_greedy(const sv_tree_t* tree, int32_t* accepted_len,
                                 int32_t* path_nodes, int32_t* out_tokens,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Same results, reading only the rows of the nodes the walk visits: step t of
- * every walk is one round (two kernel launches).  max_depth (0..4096) bounds
- * a_b: the call runs max_depth + 1 rounds and a request whose walk would
- * accept more than max_depth nodes is an input error (accepted_len -1, -1
- * slots).  The tree depth is a safe bound. */
+/* Same results, reading only the rows the walk can reach: round r takes the
+ * steps [P_r, P_(r+1)) of every walk still going, P = 0, 1, 2, 4, 8, ... (two
+ * kernel launches per round), after reading the row of each walk's current
+ * node and of its descendants down to the window's last step (rows of
+ * branches the walk does not take within the window are read but not used).
+ * max_depth (0..4096) bounds a_b: the call runs about log2(max_depth) + 2
+ * rounds, and a request whose walk would accept more than max_depth nodes is
+ * an input error (accepted_len -1, -1 slots).  The tree depth is a safe bound. */
 int32_t spec_verify_tree_greedy_early_exit(const sv_tree_t* tree, int32_t max_depth,
                                            int32_t* accepted_len, int32_t* path_nodes,
                                            int32_t* out_tokens, void* workspace,

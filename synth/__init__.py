@@ -363,8 +363,10 @@ def _tree_shape(n: int, branch: int, rng: np.random.Generator) -> np.ndarray:
 
 def make_tree_batch(cfg_id: int, device="cpu", *, B: Optional[int] = None,
                     V: Optional[int] = None, nodes=None, seed: Optional[int] = None,
-                    dtype: Optional[str] = None, p_match: Optional[float] = None) -> TreeBatch:
+                    dtype: Optional[str] = None, p_match: Optional[float] = None,
+                    branch: Optional[int] = None) -> TreeBatch:
     cfg = TREE_CONFIGS[cfg_id]
+    branch = cfg["branch"] if branch is None else int(branch)
     B = cfg["B"] if B is None else B
     V = cfg["V"] if V is None else V
     nodes = cfg["nodes"] if nodes is None else nodes
@@ -378,7 +380,7 @@ def make_tree_batch(cfg_id: int, device="cpu", *, B: Optional[int] = None,
     else:
         num_nodes = np.full(B, int(nodes), dtype=np.int32)
     N = int(num_nodes.sum())
-    parent = np.concatenate([_tree_shape(int(n), cfg["branch"], rng) for n in num_nodes]) \
+    parent = np.concatenate([_tree_shape(int(n), branch, rng) for n in num_nodes]) \
         if N else np.zeros(0, np.int64)
     g_t = _torch_gen(s_target, device)
     target = (torch.randn((N, V), generator=g_t, device=device, dtype=torch.float32)

@@ -65,6 +65,8 @@ CASES = [
     ("ragged_many_trees", 1, dict(B=1500, V=300, nodes=(1, 40))),
     ("single_node_trees", 1, dict(B=40, V=5000, nodes=1)),
     ("deep_matches", 2, dict(B=6, V=3000, p_match=1.0, nodes=60)),
+    ("chains_100_deep", 1, dict(B=4, V=500, p_match=1.0, nodes=100, branch=1)),
+    ("binary_70_deep", 1, dict(B=5, V=700, p_match=1.0, nodes=70, branch=2)),
     ("tiny_vocab", 1, dict(B=50, V=8, nodes=(1, 6))),
 ]
 
