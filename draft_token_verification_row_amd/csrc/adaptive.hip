@@ -98,6 +98,11 @@ struct GatherArgs {
   const int* count;
 };
 
+#ifndef SV_GATHER_UNROLL
+#define SV_GATHER_UNROLL 16
+#endif
+constexpr int kGatherUnroll = SV_GATHER_UNROLL;
+
 __global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs g) {
   const int gt = blockIdx.x * kBlock + threadIdx.x;
   const int nthreads = gridDim.x * kBlock;
@@ -118,7 +123,19 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(GatherArgs g) {
     const uint8_t* s = g.src + (int64_t)sr * g.src_ld * g.es;
     uint8_t* d = g.dst + (int64_t)r * g.dst_ld * g.es;
     if (g.vec) {
+      // kGatherUnroll 16-byte loads in flight per lane, then their stores (16
+      // divides a 32 KiB piece: 32 chunks per lane, two steps, no tail loop)
+      constexpr long long kStep = (long long)kWave * 16;
       long long o = p0 + (long long)lane * 16;
+      for (; o + (kGatherUnroll - 1) * kStep + 16 <= p1; o += kGatherUnroll * kStep) {
+        u32x4 v[kGatherUnroll];
+#pragma unroll
+        for (int j = 0; j < kGatherUnroll; ++j)
+          v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + o + j * kStep));
+#pragma unroll
+        for (int j = 0; j < kGatherUnroll; ++j)
+          __builtin_nontemporal_store(v[j], reinterpret_cast<u32x4*>(d + o + j * kStep));
+      }
       for (; o + 16 <= p1; o += kWave * 16) {
         const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s + o));
         __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(d + o));

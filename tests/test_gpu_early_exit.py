@@ -90,6 +90,15 @@ def test_early_exit_parity(label, cfg, kw, extra):
     assert near <= max(1, n_stoch // 100)
 
 
+def test_early_exit_largest_bound():
+    """max_k = 4096 (the largest bound): thirteen windows, the last 2048 wide,
+    on a batch whose requests are all decided in the first few."""
+    batch = synth.make_batch(5, DEV, B=30, V=7000)
+    got = run_hip(batch, max_k=4096)
+    full = run_hip(batch)
+    _assert_same_as_all_rows(batch, got, full, "max_k=4096")
+
+
 def test_early_exit_count_above_bound_is_an_input_error():
     import draft_token_verification_row_amd as sv
     batch = synth.make_batch(5, DEV, B=10, V=5000)
