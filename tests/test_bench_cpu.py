@@ -1,0 +1,44 @@
+"""Host-side pieces of bench.py (no GPU): the one-GPU guard and the accounting
+of the rows an early-exit call streams."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "GPU" in (r.stdout + r.stderr)
+
+
+def test_early_exit_windows_double():
+    for max_k in range(0, 300):
+        wins = bench.early_exit_windows(max_k)
+        assert wins[0] == (0, 1)
+        assert wins[-1][1] == max_k + 1
+        for (lo, hi), (lo2, _) in zip(wins, wins[1:]):
+            assert hi == lo2 and hi > lo
+        for r, (lo, hi) in enumerate(wins[:-1]):
+            assert hi == (1 << r)          # windows end at 1, 2, 4, 8, ...
+        assert len(wins) == (1 if max_k == 0 else max_k.bit_length() + 1)
+
+
+def test_early_exit_rows_between_exact_and_twice_exact():
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        B = int(rng.integers(1, 40))
+        k = rng.integers(0, 40, size=B)
+        acc = np.array([int(rng.integers(0, kk + 1)) for kk in k])
+        st = rng.random(B) < 0.5
+        max_k = int(k.max()) + int(rng.integers(0, 5))
+        got = bench.early_exit_rows_read(acc, k, st, max_k)
+        exact = int((acc + 1).sum() + np.minimum(acc + 1, k)[st].sum())
+        full = int((k + 1).sum() + k[st].sum())
+        assert exact <= got <= min(full, 2 * exact)
