@@ -409,6 +409,10 @@ def main():
                          "(auto: on when one call reads less than 768 MiB)")
     ap.add_argument("--launch-plan", default="auto", choices=["auto", "multi", "single"],
                     help="launch plan of the all-rows entry points (library default: auto)")
+    ap.add_argument("--shard", choices=["vocab", "request"], default=None,
+                    help="run one GPU's share of the workload split over --shards GPUs: its "
+                         "V/G columns (vocabulary-sharded logits) or its B/G requests")
+    ap.add_argument("--shards", type=int, default=1, metavar="G")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -435,7 +439,12 @@ def main():
     if args.workload == "adaptive":
         return bench_adaptive(args, sv, torch)
     cfg_id = WORKLOADS[args.workload]
-    batch = synth.make_batch(cfg_id, dev)
+    shard_kw = {}
+    if args.shard and args.shards > 1:
+        full = synth.CONFIGS[cfg_id]
+        shard_kw = {"V": full["V"] // args.shards} if args.shard == "vocab" \
+            else {"B": max(1, full["B"] // args.shards)}
+    batch = synth.make_batch(cfg_id, dev, **shard_kw)
     torch.cuda.synchronize()
 
     # Pre-built call: every buffer resident in HBM before timing.
@@ -576,7 +585,8 @@ def main():
             "logits": batch.dtype, "temperature": batch.temperature,
             "requests": ("greedy" if greedy_only else
                          f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
-            "parallelism": "single GPU",
+            "parallelism": ("single GPU" if not shard_kw else
+                            f"one GPU's share of a {args.shards}-way {args.shard} split"),
             "path": path(ee),
             "launch_plan": args.launch_plan,
         },
