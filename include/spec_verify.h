@@ -35,6 +35,8 @@
  *     by the caller.  The library allocates nothing and keeps no state between
  *     calls; calls are asynchronous on `stream` (a hipStream_t, NULL = the
  *     default stream) and results are valid once the stream reaches the call.
+ *     Outputs must not overlap the inputs, each other or the workspace; two
+ *     calls in flight at once need two workspaces.
  *   - Host-side argument checks run before any HIP call.  A failed check
  *     returns an error status and launches nothing and writes nothing.
  *   - SV_ERR_HIP reports a failed kernel launch (hipGetLastError).
