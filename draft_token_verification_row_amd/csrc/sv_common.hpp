@@ -388,6 +388,49 @@ __device__ __forceinline__ long long wave_incl_scan_ll(long long x, int lane) {
   return x;
 }
 
+// Exclusive prefix sums of two 64-bit values over one workgroup of kPlanThreads
+// threads, and their totals: wave scans, then wave 0 scans the wave totals.
+// Every thread of the workgroup must call it; s0, s1 hold kPlanWaves entries,
+// st two.  The caller separates two calls with a barrier.
+struct Scan2 {
+  long long ex0, ex1, tot0, tot1;
+};
+
+__device__ __forceinline__ Scan2 block_scan2(long long v0, long long v1, long long* s0,
+                                             long long* s1, long long* st) {
+  constexpr int kPlanWaves = kPlanThreads / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const long long i0 = wave_incl_scan_ll(v0, lane);
+  const long long i1 = wave_incl_scan_ll(v1, lane);
+  if (lane == kWave - 1) {
+    s0[wv] = i0;
+    s1[wv] = i1;
+  }
+  __syncthreads();
+  if (wv == 0) {                        // wave totals -> exclusive wave prefixes, in place
+    const long long w0 = lane < kPlanWaves ? s0[lane] : 0;
+    const long long w1 = lane < kPlanWaves ? s1[lane] : 0;
+    const long long c0 = wave_incl_scan_ll(w0, lane);
+    const long long c1 = wave_incl_scan_ll(w1, lane);
+    if (lane < kPlanWaves) {
+      s0[lane] = c0 - w0;
+      s1[lane] = c1 - w1;
+    }
+    if (lane == kPlanWaves - 1) {
+      st[0] = c0;
+      st[1] = c1;
+    }
+  }
+  __syncthreads();
+  Scan2 r;
+  r.ex0 = s0[wv] + i0 - v0;
+  r.ex1 = s1[wv] + i1 - v1;
+  r.tot0 = st[0];
+  r.tot1 = st[1];
+  return r;
+}
+
 // ------------------------------------------------------------------ k_stats
 // Persistent grid; wavefront gw takes units gw, gw + W, ...  The descriptor of
 // the next unit is fetched while the current one streams.

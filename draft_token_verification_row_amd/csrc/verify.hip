@@ -54,10 +54,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ long long s_wk[kPlanWaves];
   __shared__ long long s_ws[kPlanWaves];
+  __shared__ long long s_tot[2];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid >> 6;
   if (tid == 0) s_bad = 0;
   __syncthreads();
   const long long TB = (long long)a.K + a.B;
@@ -76,24 +75,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
     }
     const long long ks = g ? 0 : k;
-    const long long ik = wave_incl_scan_ll(k, lane);
-    const long long is = wave_incl_scan_ll(ks, lane);
-    if (lane == kWave - 1) {
-      s_wk[wv] = ik;
-      s_ws[wv] = is;
-    }
-    __syncthreads();
-    long long pk = 0, ps = 0, tot_k = 0, tot_s = 0;
-    for (int q = 0; q < kPlanWaves; ++q) {
-      if (q < wv) {
-        pk += s_wk[q];
-        ps += s_ws[q];
-      }
-      tot_k += s_wk[q];
-      tot_s += s_ws[q];
-    }
-    const long long off = carry_k + pk + ik - k;
-    const long long soff = carry_s + ps + is - ks;
+    const Scan2 sc = block_scan2(k, ks, s_wk, s_ws, s_tot);
+    const long long off = carry_k + sc.ex0;
+    const long long soff = carry_s + sc.ex1;
+    const long long tot_k = sc.tot0, tot_s = sc.tot1;
     if (b < a.B) {
       ReqInfo r;
       r.off = (int)off;
@@ -952,10 +937,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ long long s_wk[kPlanWaves];
   __shared__ long long s_wr[kPlanWaves];
+  __shared__ long long s_tot[2];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wv = tid >> 6;
   if (tid == 0) s_bad = 0;
   for (long long i = tid; i < (long long)a.K + a.B; i += kPlanThreads) a.out[i] = -1;
   for (long long i = tid; i < a.K; i += kPlanThreads) {
@@ -983,24 +967,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
     }
     const bool pair = (b < a.B) && !g && k > 0;
     const long long nr = (b < a.B) ? (pair ? 2 : 1) : 0;   // rows read in round 0
-    const long long ik = wave_incl_scan_ll(k, lane);
-    const long long ir = wave_incl_scan_ll(nr, lane);
-    if (lane == kWave - 1) {
-      s_wk[wv] = ik;
-      s_wr[wv] = ir;
-    }
-    __syncthreads();
-    long long pk = 0, pr = 0, tot_k = 0, tot_r = 0;
-    for (int q = 0; q < kPlanWaves; ++q) {
-      if (q < wv) {
-        pk += s_wk[q];
-        pr += s_wr[q];
-      }
-      tot_k += s_wk[q];
-      tot_r += s_wr[q];
-    }
-    const long long off = carry_k + pk + ik - k;
-    const long long roff = carry_r + pr + ir - nr;
+    const Scan2 sc = block_scan2(k, nr, s_wk, s_wr, s_tot);
+    const long long off = carry_k + sc.ex0;
+    const long long roff = carry_r + sc.ex1;
+    const long long tot_k = sc.tot0, tot_r = sc.tot1;
     if (b < a.B) {
       ReqInfo r;
       r.off = (int)off;
