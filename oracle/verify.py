@@ -93,7 +93,12 @@ def inverse_cdf(weights: np.ndarray, w: float):
     """Draw with one uniform w from unnormalised `weights` (reading R5).
 
     Returns (token, total, margin); margin = distance of w * total from the
-    nearer edge of the chosen token's cumulative interval, relative to total.
+    nearer edge of the chosen token's cumulative interval, in units of
+    probability mass (reading R16: the weights are p, or [p - q]_+ of two
+    distributions of total mass 1, so the comparison that picks the token
+    weighs masses of p and q, and an arithmetic that carries p and q to a
+    fixed relative precision resolves it to that precision of the unit mass,
+    not of a small residual total).
     """
     c = np.cumsum(np.asarray(weights, dtype=np.float64))   # sequential, ascending id
     total = float(c[-1])
@@ -104,7 +109,7 @@ def inverse_cdf(weights: np.ndarray, w: float):
     else:
         t = int(np.flatnonzero(weights > 0)[-1])
     lo = float(c[t - 1]) if t > 0 else 0.0
-    margin = min(abs(lo - thr), abs(float(c[t]) - thr)) / total if total > 0 else 0.0
+    margin = min(abs(lo - thr), abs(float(c[t]) - thr)) if total > 0 else 0.0
     return t, total, margin
 
 

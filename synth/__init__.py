@@ -228,6 +228,68 @@ def make_batch(cfg_id: int, device="cpu", *, B: Optional[int] = None,
         u_final=torch.as_tensor(u_final, device=device))
 
 
+RANDOM_VOCABS = (1, 2, 7, 63, 64, 65, 1000, 4099, 16385, 30011, 50000)
+
+
+def make_random_batch(seed: int, device="cpu", max_elems: int = 8 << 20) -> Batch:
+    """A batch of random shape for broad parity sweeps: dtype, vocabulary (odd,
+    tiny and multiple-of-chunk sizes), request count, ragged k_b, greedy share,
+    temperature (log-uniform in [0.05, 20]), logit scale, draft noise, strided
+    rows and masked (-inf) columns all drawn from `seed`.  Drafts are the draft
+    row's argmax with probability 1/2, else a uniform id, so that cuts fall
+    both early and late.  Rows x V stays under max_elems."""
+    rng = np.random.default_rng(np.random.SeedSequence([BASE_SEED, 7, int(seed)]))
+    dt = "f32" if rng.random() < 0.5 else "bf16"
+    V = int(rng.choice(RANDOM_VOCABS)) if rng.random() < 0.6 else int(rng.integers(1, 50001))
+    kmax = int(rng.choice([0, 1, 3, 7, 15]))
+    B = int(rng.integers(1, 33))
+    while True:
+        num_draft = rng.integers(0, kmax + 1, size=B).astype(np.int32)
+        K = int(num_draft.sum())
+        if (2 * K + B) * V <= max_elems or B == 1:
+            break
+        B = max(1, B // 2)
+    share = float(rng.choice([0.0, 0.5, 1.0]))
+    greedy = (rng.random(B) < share).astype(np.uint8)
+    T = float(np.float32(np.exp(rng.uniform(np.log(0.05), np.log(20.0)))))
+    sigma = float(rng.uniform(0.5, 4.0))
+    noise = float(rng.uniform(0.1, 2.0))
+    tdt = TORCH_DTYPE[dt]
+    target = torch.as_tensor(rng.normal(0.0, sigma, size=(K + B, V)).astype(np.float32))
+    off = np.concatenate([[0], np.cumsum(num_draft)]).astype(np.int64)
+    trow = np.concatenate([np.arange(off[b] + b, off[b] + b + num_draft[b]) for b in range(B)]
+                          + [np.zeros(0, np.int64)]).astype(np.int64)
+    draft = target[torch.as_tensor(trow)] + torch.as_tensor(
+        rng.normal(0.0, noise, size=(K, V)).astype(np.float32))
+    if V > 8 and rng.random() < 0.2:          # masked columns (never all of a row)
+        cols = rng.choice(V, size=V // 8, replace=False)
+        target[:, cols] = float("-inf")
+        draft[:, cols] = float("-inf")
+    target = target.to(tdt)
+    draft = draft.to(tdt)
+    d32 = draft.to(torch.float32)
+    amax = torch.argmax(d32, dim=1).numpy() if K else np.zeros(0, np.int64)
+    tokens = np.where(rng.random(K) < 0.5, amax, rng.integers(0, V, size=K)).astype(np.int64)
+    if K and V > 8 and bool(torch.isinf(d32[0]).any()):
+        finite = ~torch.isinf(d32).numpy()
+        for i in range(K):                     # keep tokens on unmasked ids
+            if not finite[i, tokens[i]]:
+                tokens[i] = int(amax[i])
+    ld = V + int(rng.integers(1, 18)) if rng.random() < 0.3 else V
+    b = Batch(name=f"random_{seed}", B=B, K=K, V=V, dtype=dt, num_draft=num_draft, greedy=greedy,
+              temperature=T, target=target, draft=draft,
+              tokens=torch.as_tensor(tokens).to(torch.int32),
+              u_accept=torch.as_tensor(uniforms_f32(rng, K)),
+              u_final=torch.as_tensor(uniforms_f32(rng, B))).to(device)
+    if ld != V:                               # strided rows, NaN in the pads (built on the device)
+        pt = torch.full((K + B, ld), float("nan"), dtype=tdt, device=device)
+        pt[:, :V] = b.target
+        pd = torch.full((K, ld), float("nan"), dtype=tdt, device=device)
+        pd[:, :V] = b.draft
+        b = dataclasses.replace(b, target=pt[:, :V], draft=pd[:, :V])
+    return b
+
+
 def from_arrays(target, draft, tokens, num_draft, greedy=None, temperature=None,
                 u_accept=None, u_final=None, dtype="f32", name="custom",
                 device="cpu") -> Batch:

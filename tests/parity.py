@@ -2,8 +2,9 @@
 
 Rule: per request, equal (accepted length, committed tokens) passes.  A
 stochastic request may differ only when the oracle's smallest decision margin
-(ratio tests up to the cut and the final inverse-CDF draw) is below 1e-6
-relative; such near-ties are counted and returned.  Greedy requests must
+is below 1e-6: relative for the ratio tests up to the cut, in units of
+probability mass for the final inverse-CDF draw (oracle.inverse_cdf); such
+near-ties are counted and returned.  Greedy requests must
 always match exactly.  p(y), q(y) and the residual mass must agree within
 1e-5 absolute (fp32 outputs against fp64).
 """
