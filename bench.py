@@ -194,7 +194,7 @@ def bench_tree(args, sv, torch):
         for i in range(1, len(d)):
             d[i] = d[par[int(off[b]) + i]] + 1
         depth = max(depth, max(d))
-    lib = sv._lib
+    lib = sv.lib()
     ptrs = (acc.data_ptr(), path.data_ptr(), out.data_ptr(), ws.data_ptr(), wsb, sh)
     calls = {False: lambda: lib.spec_verify_tree_greedy(ctypes.byref(tr), *ptrs),
              True: lambda: lib.spec_verify_tree_greedy_early_exit(ctypes.byref(tr), depth, *ptrs)}
@@ -303,7 +303,7 @@ def bench_adaptive(args, sv, torch):
     dev = torch.device("cuda:0")
     ab = synth.make_adaptive_batch(B=512, N=7, V=262144, dtype="bf16", device=dev)
     B, N, V = ab.B, ab.N, ab.V
-    lib = sv._lib
+    lib = sv.lib()
     nd = torch.empty(B, dtype=torch.int32, device=dev)
     off = torch.empty(B + 1, dtype=torch.int32, device=dev)
     toks = torch.empty(B * N, dtype=torch.int32, device=dev)
@@ -460,7 +460,7 @@ def main():
     bt = sv.make_batch_struct(batch.target, batch.draft, batch.tokens, nd)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    lib = sv._lib
+    lib = sv.lib()
     greedy_only = batch.temperature is None
     kmax = int(batch.num_draft.max()) if batch.K > 0 else 0
 

@@ -4,8 +4,10 @@ Argument marshalling only: every step of the verification runs in the HIP
 kernels behind the C ABI of include/spec_verify.h.  PyTorch supplies device
 memory and the current stream.  The functions carry the C names.
 
-If the library has not been built, importing this package raises ImportError:
-there is no fallback implementation.
+The library is loaded on first use (lib()), so the package and its build
+module import on a tree where libspecverify.so has not been built yet.  Any
+call made without the built library raises LibraryMissingError: there is no
+fallback implementation.
 """
 from __future__ import annotations
 
@@ -53,10 +55,15 @@ class SvTree(ctypes.Structure):
     ]
 
 
+class LibraryMissingError(ImportError):
+    """libspecverify.so has not been built (no fallback path exists)."""
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        raise LibraryMissingError(
+            f"{LIB_PATH} is missing: build it with `python draft_token_verification_row_amd/build.py` "
+            "(or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.spec_verify_workspace_bytes.argtypes = [i32, i32, i32]
@@ -95,7 +102,23 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on the first call; raises LibraryMissingError
+    when it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    # `_lib` stays available as an attribute for callers of the raw C functions
+    if name == "_lib":
+        return lib()
+    raise AttributeError(name)
 
 
 class SpecVerifyError(RuntimeError):
@@ -123,22 +146,22 @@ def _stream_handle(stream) -> Optional[int]:
 
 
 def spec_verify_workspace_bytes(B: int, K: int, V: int) -> int:
-    return int(_lib.spec_verify_workspace_bytes(B, K, V))
+    return int(lib().spec_verify_workspace_bytes(B, K, V))
 
 
 def spec_verify_status_string(status: int) -> str:
-    return _lib.spec_verify_status_string(status).decode()
+    return lib().spec_verify_status_string(status).decode()
 
 
 def spec_verify_set_launch_plan(plan: int) -> None:
     """0 automatic, 1 multi-kernel pipeline, 2 single launch (calling thread only)."""
-    st = _lib.spec_verify_set_launch_plan(int(plan))
+    st = lib().spec_verify_set_launch_plan(int(plan))
     if st != SV_OK:
         raise SpecVerifyError(st)
 
 
 def spec_verify_set_profile_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
-    return int(_lib.spec_verify_set_profile_events(ev_begin, ev_end))
+    return int(lib().spec_verify_set_profile_events(ev_begin, ev_end))
 
 
 def make_batch_struct(target: torch.Tensor, draft: Optional[torch.Tensor],
@@ -180,10 +203,10 @@ def spec_verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, num_dra
         out_tokens = torch.empty(bt.K + bt.B, dtype=torch.int32, device=dev)
     workspace, wsb = _workspace(bt.B, bt.K, bt.V, workspace, dev)
     if max_k is None:
-        st = _lib.spec_verify_greedy(ctypes.byref(bt), _ptr(accepted_len), _ptr(out_tokens),
+        st = lib().spec_verify_greedy(ctypes.byref(bt), _ptr(accepted_len), _ptr(out_tokens),
                                      _ptr(workspace), wsb, _stream_handle(stream))
     else:
-        st = _lib.spec_verify_greedy_early_exit(ctypes.byref(bt), int(max_k), _ptr(accepted_len),
+        st = lib().spec_verify_greedy_early_exit(ctypes.byref(bt), int(max_k), _ptr(accepted_len),
                                                 _ptr(out_tokens), _ptr(workspace), wsb,
                                                 _stream_handle(stream))
     if st != SV_OK:
@@ -221,9 +244,9 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
             _ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(resid_mass),
             _ptr(workspace), wsb, _stream_handle(stream))
     if max_k is None:
-        st = _lib.spec_verify_sample(ctypes.byref(bt), *rest)
+        st = lib().spec_verify_sample(ctypes.byref(bt), *rest)
     else:
-        st = _lib.spec_verify_sample_early_exit(ctypes.byref(bt), int(max_k), *rest)
+        st = lib().spec_verify_sample_early_exit(ctypes.byref(bt), int(max_k), *rest)
     if st != SV_OK:
         raise SpecVerifyError(st)
     return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,
@@ -240,7 +263,7 @@ def spec_verify_accept_stats(accepted_len: torch.Tensor, num_draft: torch.Tensor
         raise ValueError("accepted_len and num_draft must have the same length")
     if out is None:
         out = torch.empty(4 + max_pos, dtype=torch.float64, device=accepted_len.device)
-    st = _lib.spec_verify_accept_stats(_ptr(accepted_len), _ptr(num_draft), B, max_pos, _ptr(out),
+    st = lib().spec_verify_accept_stats(_ptr(accepted_len), _ptr(num_draft), B, max_pos, _ptr(out),
                                        _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st)
@@ -248,7 +271,7 @@ def spec_verify_accept_stats(accepted_len: torch.Tensor, num_draft: torch.Tensor
 
 
 def spec_verify_tree_workspace_bytes(B: int, N: int, V: int) -> int:
-    return int(_lib.spec_verify_tree_workspace_bytes(B, N, V))
+    return int(lib().spec_verify_tree_workspace_bytes(B, N, V))
 
 
 def make_tree_struct(target: torch.Tensor, parent: torch.Tensor, tokens: torch.Tensor,
@@ -289,9 +312,9 @@ def spec_verify_tree_greedy(target: torch.Tensor, parent: torch.Tensor, tokens: 
     ptrs = (_ptr(accepted_len), _ptr(path_nodes), _ptr(out_tokens), _ptr(workspace), wsb,
             _stream_handle(stream))
     if max_depth is None:
-        st = _lib.spec_verify_tree_greedy(ctypes.byref(tr), *ptrs)
+        st = lib().spec_verify_tree_greedy(ctypes.byref(tr), *ptrs)
     else:
-        st = _lib.spec_verify_tree_greedy_early_exit(ctypes.byref(tr), int(max_depth), *ptrs)
+        st = lib().spec_verify_tree_greedy_early_exit(ctypes.byref(tr), int(max_depth), *ptrs)
     if st != SV_OK:
         raise SpecVerifyError(st)
     return accepted_len, path_nodes, out_tokens
@@ -326,7 +349,7 @@ def spec_verify_adaptive_length(conf: torch.Tensor, cost: torch.Tensor, draft_to
     toks = torch.empty(max(B * N, 1), dtype=torch.int32, device=dev)
     src = torch.empty(max(B * N, 1), dtype=torch.int32, device=dev) if want_src_index else None
     prog = torch.empty(B, dtype=torch.float64, device=dev) if want_progress else None
-    st = _lib.spec_verify_adaptive_length(B, N, _ptr(conf), _ptr(cost), _ptr(draft_tokens),
+    st = lib().spec_verify_adaptive_length(B, N, _ptr(conf), _ptr(cost), _ptr(draft_tokens),
                                           _ptr(nd), _ptr(off), _ptr(toks), _ptr(src), _ptr(prog),
                                           _stream_handle(stream))
     if st != SV_OK:
@@ -340,7 +363,7 @@ def spec_verify_gather_rows(src: torch.Tensor, index: torch.Tensor, count: torch
     ld = _rows(src, "src")
     if out is None:
         out = torch.empty(max(max_rows, 1), src.shape[1], dtype=src.dtype, device=src.device)
-    st = _lib.spec_verify_gather_rows(_DTYPES[src.dtype], int(src.shape[1]), _ptr(src), ld,
+    st = lib().spec_verify_gather_rows(_DTYPES[src.dtype], int(src.shape[1]), _ptr(src), ld,
                                       int(src.shape[0]), _ptr(index), _ptr(count), int(max_rows),
                                       _ptr(out), _rows(out, "out"), _stream_handle(stream))
     if st != SV_OK:

@@ -16,8 +16,8 @@ LIB = os.path.join(ROOT, "draft_token_verification_row_amd", "libspecverify.so")
 @pytest.fixture(scope="module")
 def sv():
     if not os.path.exists(LIB):
-        from draft_token_verification_row_amd import build as b
-        b.build(verbose=False)
+        import __graft_entry__
+        __graft_entry__._build_module().build(verbose=False)
     import draft_token_verification_row_amd as m
     return m
 
@@ -82,19 +82,19 @@ def _batch(sv, **kw):
 def _sample(sv, bt, T=1.0, ws_bytes=None, ws=FAKE, ua=FAKE, uf=FAKE, acc=FAKE, out=FAKE):
     need = sv.spec_verify_workspace_bytes(max(bt.B, 1), max(bt.K, 0), max(bt.V, 1))
     wsb = need if ws_bytes is None else ws_bytes
-    return sv._lib.spec_verify_sample(ctypes.byref(bt), ctypes.c_float(T), None, ua, uf, acc, out,
+    return sv.lib().spec_verify_sample(ctypes.byref(bt), ctypes.c_float(T), None, ua, uf, acc, out,
                                       None, None, None, ws, wsb, None)
 
 
 def _greedy(sv, bt, ws_bytes=None, ws=FAKE, acc=FAKE, out=FAKE):
     need = sv.spec_verify_workspace_bytes(max(bt.B, 1), max(bt.K, 0), max(bt.V, 1))
     wsb = need if ws_bytes is None else ws_bytes
-    return sv._lib.spec_verify_greedy(ctypes.byref(bt), acc, out, ws, wsb, None)
+    return sv.lib().spec_verify_greedy(ctypes.byref(bt), acc, out, ws, wsb, None)
 
 
 def test_host_validation_rejects_bad_arguments(sv):
     INV, UNS, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED, sv.SV_ERR_WORKSPACE
-    assert sv._lib.spec_verify_sample(None, ctypes.c_float(1.0), None, FAKE, FAKE, FAKE, FAKE,
+    assert sv.lib().spec_verify_sample(None, ctypes.c_float(1.0), None, FAKE, FAKE, FAKE, FAKE,
                                       None, None, None, FAKE, 1 << 20, None) == INV
     assert _sample(sv, _batch(sv, B=0)) == INV
     assert _sample(sv, _batch(sv, K=-1)) == INV
@@ -166,7 +166,7 @@ def torch_equal(a, b):
 
 def test_accept_stats_host_validation(sv):
     INV = sv.SV_ERR_INVALID_ARG
-    f = sv._lib.spec_verify_accept_stats
+    f = sv.lib().spec_verify_accept_stats
     assert f(None, FAKE, 4, 3, FAKE, None) == INV
     assert f(FAKE, None, 4, 3, FAKE, None) == INV
     assert f(FAKE, FAKE, 4, 3, None, None) == INV
@@ -178,8 +178,8 @@ def test_accept_stats_host_validation(sv):
 def test_early_exit_host_validation(sv):
     INV, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_WORKSPACE
     need = sv.spec_verify_workspace_bytes(4, 8, 1000)
-    g = sv._lib.spec_verify_greedy_early_exit
-    s = sv._lib.spec_verify_sample_early_exit
+    g = sv.lib().spec_verify_greedy_early_exit
+    s = sv.lib().spec_verify_sample_early_exit
 
     def smp(bt, max_k, T=1.0, wsb=need, ua=FAKE):
         return s(ctypes.byref(bt), max_k, ctypes.c_float(T), None, ua, FAKE, FAKE, FAKE, None,
@@ -212,8 +212,8 @@ def test_tree_host_validation(sv):
     assert sv.spec_verify_tree_workspace_bytes(2, 1, 1000) == 0      # N < B
     assert sv.spec_verify_tree_workspace_bytes(0, 1, 1000) == 0
     assert sv.spec_verify_tree_workspace_bytes(1, 1, 0) == 0
-    g = sv._lib.spec_verify_tree_greedy
-    e = sv._lib.spec_verify_tree_greedy_early_exit
+    g = sv.lib().spec_verify_tree_greedy
+    e = sv.lib().spec_verify_tree_greedy_early_exit
 
     def call(tr, wsb=need, acc=FAKE, path=FAKE, out=FAKE, ws=FAKE):
         return g(ctypes.byref(tr) if tr is not None else None, acc, path, out, ws, wsb, None)
@@ -265,7 +265,7 @@ def test_tree_synthetic_shapes():
 
 def test_adaptive_and_gather_host_validation(sv):
     INV, UNS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED
-    f = sv._lib.spec_verify_adaptive_length
+    f = sv.lib().spec_verify_adaptive_length
     assert f(0, 7, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
     assert f(4, -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
     assert f(4, 4097, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == INV
@@ -275,7 +275,7 @@ def test_adaptive_and_gather_host_validation(sv):
     assert f(4, 7, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, None) == INV
     assert f(4, 7, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None) == INV
     assert f(4, 7, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == INV
-    g = sv._lib.spec_verify_gather_rows
+    g = sv.lib().spec_verify_gather_rows
     assert g(5, 100, FAKE, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == UNS
     assert g(1, 0, FAKE, 100, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
     assert g(1, 100, FAKE, 99, 4, FAKE, FAKE, 4, FAKE, 100, None) == INV
@@ -290,6 +290,6 @@ def test_adaptive_and_gather_host_validation(sv):
 
 def test_launch_plan_values(sv):
     for bad in (-1, 3, 99):
-        assert sv._lib.spec_verify_set_launch_plan(bad) == sv.SV_ERR_INVALID_ARG
+        assert sv.lib().spec_verify_set_launch_plan(bad) == sv.SV_ERR_INVALID_ARG
     for ok in (1, 2, 0):
-        assert sv._lib.spec_verify_set_launch_plan(ok) == sv.SV_OK
+        assert sv.lib().spec_verify_set_launch_plan(ok) == sv.SV_OK

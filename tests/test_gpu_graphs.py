@@ -101,7 +101,7 @@ def test_tree_and_adaptive_in_graph():
     res = sv.spec_verify_adaptive_length(ab.conf, ab.cost, ab.tokens)
 
     def call_a():
-        st = sv._lib.spec_verify_adaptive_length(
+        st = sv.lib().spec_verify_adaptive_length(
             64, 7, ab.conf.data_ptr(), ab.cost.data_ptr(), ab.tokens.data_ptr(),
             res["num_draft"].data_ptr(), res["offsets"].data_ptr(), res["tokens"].data_ptr(),
             res["src_index"].data_ptr(), res["progress"].data_ptr(),
