@@ -78,7 +78,9 @@ def keeps_draft(u: float, p_y: float, q_y: float) -> bool:
 
 
 def accept_margin(u: float, p_y: float, q_y: float) -> float:
-    """Relative distance of the ratio test from its decision boundary."""
+    """Relative distance of the ratio test u * q(y) < p(y) from its boundary:
+    |u q(y) - p(y)| / max(u q(y), p(y)); 1 when both sides are 0 (decided
+    exactly).  A mismatch on a test closer than 1e-6 is a near-tie."""
     a, b = float(u) * q_y, p_y
     top = max(a, b)
     return 1.0 if top == 0.0 else abs(a - b) / top
@@ -92,13 +94,11 @@ def positive_residual(p: np.ndarray, q: np.ndarray) -> np.ndarray:
 def inverse_cdf(weights: np.ndarray, w: float):
     """Draw with one uniform w from unnormalised `weights` (reading R5).
 
-    Returns (token, total, margin); margin = distance of w * total from the
-    nearer edge of the chosen token's cumulative interval, in units of
-    probability mass (reading R16: the weights are p, or [p - q]_+ of two
-    distributions of total mass 1, so the comparison that picks the token
-    weighs masses of p and q, and an arithmetic that carries p and q to a
-    fixed relative precision resolves it to that precision of the unit mass,
-    not of a small residual total).
+    Returns (token, total, margin).  The margin is the distance of w * total
+    from the nearer edge of the chosen token's cumulative interval
+    [C_(t-1), C_t], relative to the total, so it does not depend on the scale
+    of the weights (a residual [p - q]_+ of total 1e-9 and one of total 0.5
+    with the same shape have the same margin).
     """
     c = np.cumsum(np.asarray(weights, dtype=np.float64))   # sequential, ascending id
     total = float(c[-1])
@@ -109,7 +109,7 @@ def inverse_cdf(weights: np.ndarray, w: float):
     else:
         t = int(np.flatnonzero(weights > 0)[-1])
     lo = float(c[t - 1]) if t > 0 else 0.0
-    margin = min(abs(lo - thr), abs(float(c[t]) - thr)) if total > 0 else 0.0
+    margin = min(abs(lo - thr), abs(float(c[t]) - thr)) / total if total > 0 else 0.0
     return t, total, margin
 
 

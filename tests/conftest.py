@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    parity = sys.modules.get("tests.parity")
+    ties = getattr(parity, "NEAR_TIES", None)
+    if ties is None:
+        return
+    terminalreporter.write_line(
+        f"near-ties (GPU != oracle with the oracle's deciding margin < 1e-6 relative): {len(ties)}")
+    for label, b, m in ties[:50]:
+        terminalreporter.write_line(f"  {label} request {b}: margin {m:.3e}")

@@ -311,9 +311,65 @@ def pin_packed_batch(vm):
     assert np.all(res["resid_mass"][[0, 3]] > 0) and res["resid_mass"][1] == -1.0
 
 
+# ---------------------------------------------------------------- decision margins
+def pin_decision_margins(vm):
+    """The margins that decide which GPU/oracle disagreements count as
+    near-ties, against hand-derived values.
+
+    Ratio test: |u q - p| / max(u q, p).  Draw: distance of w * total from the
+    nearer edge of the chosen token's cumulative interval, relative to the
+    total.  A request's margin is the smallest over the ratio tests up to and
+    including its cut plus the final draw (later positions decide nothing)."""
+    am = vm.accept_margin
+    for (u, p, q), want in (((0.5, 0.1, 0.4), 0.5),         # 0.2 vs 0.1
+                            ((0.25, 0.1, 0.4), 0.0),        # 0.1 vs 0.1 exactly
+                            ((0.9, 0.3, 0.3), 0.1),         # 0.27 vs 0.3
+                            ((0.5, 0.3, 0.1), 0.25 / 0.3),  # 0.05 vs 0.3
+                            ((0.5, 1e-13, 4e-13), 0.5),     # scale free
+                            ((0.5, 0.0, 0.0), 1.0)):        # 0 vs 0: decided exactly
+        got = am(u, p, q)
+        assert abs(got - want) <= 1e-12, ((u, p, q), got, want)
+    # weights 1 2 3 4: cumulative 1 3 6 10, total 10
+    W = np.array([1.0, 2.0, 3.0, 4.0])
+    for w, tok, want in ((0.375, 2, 0.075),     # 3.75 in [3, 6): lower edge nearer
+                         (0.5625, 2, 0.0375),   # 5.625 in [3, 6): upper edge nearer
+                         (0.25, 1, 0.05),       # 2.5 in [1, 3)
+                         (0.0, 0, 0.0),         # 0 on the lower edge of token 0
+                         (0.95, 3, 0.05)):      # 9.5 in [6, 10)
+        for scale in (1.0, 2.0 ** -30, 2.0 ** 20):     # relative to the total
+            t, total, m = vm.inverse_cdf(W * scale, w)
+            assert t == tok and abs(total - 10.0 * scale) <= 1e-12 * scale, (w, scale, t, total)
+            assert abs(m - want) <= 1e-12, (w, scale, m, want)
+    # zero-weight ids: cumulative 0 2 2 4
+    t, _, m = vm.inverse_cdf(np.array([0.0, 2.0, 0.0, 2.0]), 0.25)
+    assert t == 1 and abs(m - 0.25) <= 1e-12, (t, m)
+    t, _, m = vm.inverse_cdf(np.array([0.0, 2.0, 0.0, 2.0]), 0.5)
+    assert t == 3 and m == 0.0, (t, m)
+    # request: p0 = .1 .2 .3 .4, q0 = .4 .3 .2 .1, y0 = 0, u0 = .5 -> reject
+    # (margin .5); residual 0 0 .1 .3 (Z = .4), w = .5 -> 0.2 in [.1, .4)
+    # -> token 3, margin min(.1, .2)/.4 = .25.  Position 1 (after the cut) has
+    # a test 0.0099 from its boundary that decides nothing.
+    tgt = _logits_from_probs([[0.1, 0.2, 0.3, 0.4], [0.25] * 4, [0.7, 0.1, 0.1, 0.1]])
+    dr = _logits_from_probs([[0.4, 0.3, 0.2, 0.1], [0.5, 0.2, 0.2, 0.1]])
+    r = _run(vm, tgt, dr, [0, 0], False, 1.0, [0.5, 0.505], 0.5)
+    assert r["a"] == 0 and r["committed"] == [3], r
+    assert abs(r["resid_mass"] - 0.4) <= 1e-12, r
+    assert abs(r["margin"] - 0.25) <= 1e-9, r["margin"]
+    # u0 = .9: reject with margin |.36 - .1| / .36; the draw margin (.25) is smaller
+    r = _run(vm, tgt, dr, [0, 0], False, 1.0, [0.9, 0.505], 0.5)
+    assert r["a"] == 0 and abs(r["margin"] - 0.25) <= 1e-9, r
+    # u0 = .2: reject on the boundary itself (.08 vs .1 keeps: .2 * .4 = .08 < .1)
+    # -> kept; u1 = .505 rejects position 1 (.2525 vs .25, margin .0099)
+    r = _run(vm, tgt, dr, [0, 0], False, 1.0, [0.2, 0.505], 0.5)
+    assert r["a"] == 1, r
+    assert abs(r["margin"] - (0.2525 - 0.25) / 0.2525) <= 1e-9, r["margin"]
+    # greedy requests have no margin
+    assert math.isinf(_run(vm, tgt, None, [3, 0], True, None, [0, 0], 0.5)["margin"])
+
+
 ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ties,
             pin_exact_distribution_quadrature, pin_special_cases, pin_greedy_invariants,
-            pin_packed_batch]
+            pin_packed_batch, pin_decision_margins]
 
 
 # ---------------------------------------------------------------- acceptance statistics

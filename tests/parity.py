@@ -2,11 +2,11 @@
 
 Rule: per request, equal (accepted length, committed tokens) passes.  A
 stochastic request may differ only when the oracle's smallest decision margin
-is below 1e-6: relative for the ratio tests up to the cut, in units of
-probability mass for the final inverse-CDF draw (oracle.inverse_cdf); such
-near-ties are counted and returned.  Greedy requests must
-always match exactly.  p(y), q(y) and the residual mass must agree within
-1e-5 absolute (fp32 outputs against fp64).
+is below 1e-6 relative (the ratio tests up to the cut, relative to the larger
+side; the final inverse-CDF draw, relative to the total of its weights);
+such near-ties are counted, returned and reported at the end of the session.
+Greedy requests must always match exactly.  p(y), q(y) and the residual mass
+must agree within 1e-5 absolute (fp32 outputs against fp64).
 """
 from __future__ import annotations
 
@@ -18,6 +18,8 @@ import synth
 
 NEAR_TIE = 1e-6
 PROB_TOL = 1e-5
+# (label, request, oracle margin) of every near-tie met in this process
+NEAR_TIES = []
 
 
 def run_hip(batch: synth.Batch, **kw) -> dict:
@@ -50,6 +52,8 @@ def compare(batch: synth.Batch, got: dict, ref: dict, label: str = "") -> int:
         if batch.greedy[b] or not (ref["margin"][b] < NEAR_TIE):
             raise AssertionError(msg)
         near += 1
+        NEAR_TIES.append((label, b, float(ref["margin"][b])))
+        print(f"near-tie: {msg}", flush=True)
     if batch.temperature is not None and got.get("p_draft") is not None:
         stoch_rows = np.repeat(batch.greedy == 0, nd)
         for name in ("p_draft", "q_draft"):

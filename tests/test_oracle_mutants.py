@@ -1,7 +1,8 @@
 """Planted mistakes in the oracle (CPU only) must each fail at least one pin.
 
 This shows the pins constrain every step: the ratio test, the residual, the
-inverse CDF, the temperature, the tie rule, row/operand indexing and the cut.
+inverse CDF, the temperature, the tie rule, row/operand indexing and the cut,
+and the decision margins that classify GPU/oracle disagreements as near-ties.
 """
 import numpy as np
 import pytest
@@ -65,7 +66,46 @@ def _no_cut(target_rows, draft_rows, tokens, greedy, T, u, w):
     return r
 
 
+def _cdf_margin(edge_shift_lo=0, edge_shift_hi=0, scale=False, zero=False):
+    """inverse_cdf with a mistaken margin: wrong interval edge, absolute
+    instead of relative to the total, or always 0."""
+    def f(weights, w):
+        t, total, m = _orig_cdf(weights, w)
+        c = np.concatenate([[0.0], np.cumsum(np.asarray(weights, np.float64))])
+        thr = float(w) * total
+        lo = c[min(max(t + edge_shift_lo, 0), len(c) - 1)]
+        hi = c[min(max(t + 1 + edge_shift_hi, 0), len(c) - 1)]
+        m = min(abs(lo - thr), abs(hi - thr)) / (1.0 if scale else total) if total > 0 else 0.0
+        return t, total, 0.0 if zero else m
+    return f
+
+
+def _request_margin(mode):
+    """verify_request whose margin leaves out the draw ("tests") or also takes
+    the ratio tests after the cut ("all")."""
+    def f(target_rows, draft_rows, tokens, greedy, T, u, w):
+        r = _orig_request(target_rows, draft_rows, tokens, greedy, T, u, w)
+        if greedy or len(tokens) == 0:
+            return r
+        k, a = len(tokens), r["a"]
+        ms = [vm.accept_margin(u[i], r["p_y"][i], r["q_y"][i]) for i in range(k)]
+        if mode == "tests":
+            m = min(ms[:min(a + 1, k)])
+        else:
+            m = min([r["margin"]] + ms)
+        return dict(r, margin=m)
+    return f
+
+
 MUTANTS = {
+    "accept_margin_zero": ("accept_margin", lambda u, p, q: 0.0),
+    "accept_margin_absolute": ("accept_margin", lambda u, p, q: abs(float(u) * q - p)),
+    "draw_margin_zero": ("inverse_cdf", _cdf_margin(zero=True)),
+    "draw_margin_absolute": ("inverse_cdf", _cdf_margin(scale=True)),
+    "draw_margin_next_upper_edge": ("inverse_cdf", _cdf_margin(edge_shift_hi=1)),
+    "draw_margin_previous_lower_edge": ("inverse_cdf", _cdf_margin(edge_shift_lo=-1)),
+    "request_margin_without_draw": ("verify_request", _request_margin("tests")),
+    "request_margin_after_cut": ("verify_request", _request_margin("all")),
     "accept_le": ("keeps_draft", lambda u, p, q: float(u) * q <= p),
     "accept_swapped": ("keeps_draft", lambda u, p, q: float(u) * p < q),
     "accept_inverted": ("keeps_draft", lambda u, p, q: float(u) * q > p),

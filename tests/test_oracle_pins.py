@@ -41,6 +41,10 @@ def test_cost_model_illustration():
     pins.pin_cost_model()
 
 
+def test_decision_margins():
+    pins.pin_decision_margins(vm)
+
+
 def test_packed_ragged_batch():
     pins.pin_packed_batch(vm)
 
