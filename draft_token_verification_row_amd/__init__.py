@@ -132,11 +132,11 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _rows(t: torch.Tensor, name: str):
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.stride(1) != 1 and t.numel() > 0):
         raise ValueError(f"{name} must be 2-D with unit stride along the vocabulary")
     if t.dtype not in _DTYPES:
         raise ValueError(f"{name} dtype {t.dtype} unsupported (float32 or bfloat16)")
-    return t.stride(0)
+    return max(t.stride(0), t.shape[1]) if t.numel() == 0 else t.stride(0)
 
 
 def _stream_handle(stream) -> Optional[int]:

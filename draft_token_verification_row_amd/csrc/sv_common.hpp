@@ -137,6 +137,7 @@ struct Args {
   float* resid_out;
   float c;            // fl(log2(e)/T): the scale of every exponent
   double c64;         // the same value in fp64
+  double T64;         // the fp32 temperature, widened (the fp64 draw divides by it)
   const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
   const int* rowcount;       // number of rows in rowlist
   int ee_round;              // early-exit round, -1 on the all-rows path

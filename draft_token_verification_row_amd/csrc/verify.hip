@@ -251,8 +251,6 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
     if (!upper && i < k) {
       if (g) {
         rej = (y != amax);
-        if (a.p_out) a.p_out[drow0 + i] = -1.f;   // no probabilities for greedy rows
-        if (a.q_out) a.q_out[drow0 + i] = -1.f;
       } else if (!yok) {
         invalid = true;
         if (a.p_out) a.p_out[drow0 + i] = -1.f;
@@ -291,6 +289,14 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
       amaxA = __shfl(amax, src);
     }
     if (g && found) break;
+  }
+  if (g) {
+    // no probabilities for greedy rows: every position, also those after the
+    // cut that the loop above never reached
+    for (int i = lane; i < k; i += kWave) {
+      if (a.p_out) a.p_out[drow0 + i] = -1.f;
+      if (a.q_out) a.q_out[drow0 + i] = -1.f;
+    }
   }
   if (__any(invalid) || no_mass) {
     for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
@@ -612,10 +618,14 @@ __device__ __forceinline__ void unit_weights(const typename L::Elem* tp, const t
 // weights in registers for that walk; otherwise they are recomputed (same
 // values, fewer registers).  In a block larger than kBlock the extra threads
 // take part in the barriers only, so the result is the same for any block size.
+// The thread that returns the token also stores in *margin the distance of
+// thr from the nearer edge of that token's cumulative interval (in the units of
+// the weights), or -1 when no id crossed thr and the last id with weight was
+// taken instead.
 template <class L, int PER, bool KEEP, class WF>
 __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* dp, int s0,
                            int s1, int y, const WF& wf, double before, double thr, int fallback,
-                           double* s_wave, int* s_owner) {
+                           double* s_wave, int* s_owner, double* margin) {
   constexpr int E = L::E;
   static_assert(PER % E == 0, "per-thread ids must be whole chunks");
   const int tid = threadIdx.x;
@@ -677,12 +687,14 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
         for (int e = 0; e < E; ++e)
           if (w[e] > 0.f) tok = v0 + c * E + e;
       }
+      *margin = -1.0;
       return tok;
     }
     return -2;
   }
   if (tid != owner) return -2;
   double cum = excl;
+  double lo = 0.0, hi = 0.0;
   int tok = -1, last = -1;
 #pragma unroll
   for (int c = 0; c < PER / E; ++c) {
@@ -690,19 +702,202 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
     chunk(c, w);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
+      const double prev = cum;
       cum += (double)w[e];
       if (w[e] > 0.f) last = v0 + c * E + e;
-      if (tok < 0 && cum > thr) tok = v0 + c * E + e;
+      if (tok < 0 && cum > thr) {
+        tok = v0 + c * E + e;
+        lo = prev;
+        hi = cum;
+      }
     }
   }
+  *margin = tok >= 0 ? fmin(thr - lo, hi - thr) : -1.0;
   return tok >= 0 ? tok : last;
 }
+
+// ------------------------------------------------------------------ certified draw
+// The draw above evaluates the weights in fp32 (exp2 with the fp32 scale c, so
+// at the temperature log2(e)/c; reciprocals of the row sums rounded to fp32;
+// lane sums of a few dozen fp32 terms) and locates the crossing of w * Z in
+// fp64 over them.  Its cumulative masses then differ from the exact ones at
+// temperature T by less than about 1.1e-5 of probability mass in the worst
+// case (temperature 2^-24 relative, <= 2 ln(V) * 2^-24 per row; rounding and
+// exp2 <= 2^-20; row sums <= 40 * 2^-24 relative per row).  A draw whose
+// crossing lies farther than kCertMargin from both edges of the chosen id's
+// interval is therefore the exact draw.  Otherwise (a crossing closer than
+// that, no crossing found, or a residual total that rounded to 0) the whole
+// workgroup redoes the draw from the logits in fp64: p_v = exp((z_v - M)/T)/S
+// with S summed in fp64, the residual [p_v - q_v]_+ formed from those fp64
+// values (no cancellation to speak of at any residual total), its total, and
+// the first id whose running sum exceeds w times that total.  Such draws are
+// rare (a margin below 2^-15 of a residual total Z happens with probability
+// about 2^-14 / Z) and take several fp64 passes over the row pair on one CU.
+constexpr double kCertMargin = 0x1p-15;
+constexpr int kFusedWavesMax = 16;      // largest workgroup that runs a draw: 1024 threads
 
 struct FinalizeShared {
   double wave[kWavesPerBlock];
   double before, thr, Z;
   int unit, mode, fallback, owner;
+  int tok, cert;                  // the fp32 draw and whether its margin certifies it
+  double red[kFusedWavesMax];     // fp64 draw: wave totals of a block scan or sum
+  int ptok, found, plast;
 };
+
+// Sum of x over the workgroup, in the same order in every thread.
+__device__ double block_sum(double x, double* red) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  x = wave_sum(x);
+  __syncthreads();                      // red may still be read by an earlier call
+  if (lane == 0) red[wv] = x;
+  __syncthreads();
+  double t = 0.0;
+  for (int q = 0; q < nw; ++q) t += red[q];
+  return t;
+}
+
+// fp64 weight of one id: p_v, or [p_v - q_v]_+ when dp rows are given.
+struct PreciseW {
+  double Mp, Mq, Sp, Sq, T;
+  bool resid;
+  __device__ __forceinline__ double operator()(float z, float d) const {
+    const double p = exp(((double)z - Mp) / T) / Sp;
+    if (!resid) return p;
+    const double q = exp(((double)d - Mq) / T) / Sq;
+    return fmax(p - q, 0.0);
+  }
+};
+
+// Visit the ids [v0, v0 + n) of a target row (and of a draft row when dp is
+// not null) in ascending order: f(id, z, d).  Whole chunks use the vector
+// loads of L (v0 a multiple of L::E), the rest single elements.
+template <class L, class F>
+__device__ __forceinline__ void visit_ids(const typename L::Elem* tp, const typename L::Elem* dp,
+                                          int v0, int n, F& f) {
+  constexpr int E = L::E;
+  int v = v0;
+  for (; v + E <= v0 + n; v += E) {
+    float vt[E], vd[E];
+    L::unpack(L::load(tp + v), vt);
+    if (dp) L::unpack(L::load(dp + v), vd);
+#pragma unroll
+    for (int e = 0; e < E; ++e) f(v + e, vt[e], dp ? vd[e] : 0.f);
+  }
+  for (; v < v0 + n; ++v) f(v, L::one(tp + v), dp ? L::one(dp + v) : 0.f);
+}
+
+// The draw in fp64 by the whole workgroup (every thread calls it; the result
+// is valid in every thread).  resid: weights [p - q]_+ (falling back to p if
+// their total is 0), else p.  Returns the token; *Z = total of the residual
+// weights (0 after the fallback) or of p.
+template <class L>
+__device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* dp, int V,
+                            double Mp, double Mq, double T, double w, bool resid, double* Z,
+                            FinalizeShared& sh) {
+  constexpr int E = L::E;
+  constexpr int SLOT = E * 4;           // consecutive ids per thread and tile
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
+  const int nslot = (V + SLOT - 1) / SLOT;
+  // row sums
+  PreciseW pw;
+  pw.Mp = Mp;
+  pw.Mq = Mq;
+  pw.T = T;
+  double sp = 0.0, sq = 0.0;
+  auto sums = [&](int, float z, float d) {
+    sp += exp(((double)z - Mp) / T);
+    if (resid) sq += exp(((double)d - Mq) / T);
+  };
+  for (int sl = tid; sl < nslot; sl += nthr)
+    visit_ids<L>(tp, resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), sums);
+  pw.Sp = block_sum(sp, sh.red);
+  pw.Sq = resid ? block_sum(sq, sh.red) : 1.0;
+  // totals of the residual and of p
+  pw.resid = resid;
+  double tr = 0.0, tq = 0.0;
+  PreciseW pp = pw;
+  pp.resid = false;
+  auto totals = [&](int, float z, float d) {
+    tq += pp(z, d);
+    if (resid) tr += pw(z, d);
+  };
+  for (int sl = tid; sl < nslot; sl += nthr)
+    visit_ids<L>(tp, resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), totals);
+  const double Ptot = block_sum(tq, sh.red);
+  double total = Ptot;
+  if (resid) {
+    const double Ztot = block_sum(tr, sh.red);
+    if (Ztot > 0.0) total = Ztot;
+    else pw.resid = false;              // p == q: draw from p
+    *Z = Ztot > 0.0 ? Ztot : 0.0;
+  } else {
+    *Z = Ptot;
+  }
+  const double thr = w * total;
+  // first id whose running sum exceeds thr, tile by tile (nthr slots a tile)
+  if (tid == 0) {
+    sh.found = 0;
+    sh.plast = -1;
+  }
+  double carry = 0.0;
+  int mylast = -1;
+  for (int base = 0; base < nslot; base += nthr) {
+    const int sl = base + tid;
+    double ts = 0.0;
+    int tl = -1;
+    auto acc = [&](int v, float z, float d) {
+      const double x = pw(z, d);
+      ts += x;
+      if (x > 0.0) tl = v;
+    };
+    if (sl < nslot) visit_ids<L>(tp, pw.resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), acc);
+    if (tl >= 0) mylast = tl;
+    const double iw = wave_incl_scan(ts, lane);
+    __syncthreads();
+    if (lane == kWave - 1) sh.red[wv] = iw;
+    if (tid == 0) sh.owner = INT_MAX;
+    __syncthreads();
+    double pre = 0.0, tile = 0.0;
+    for (int q = 0; q < (nthr >> 6); ++q) {
+      if (q < wv) pre += sh.red[q];
+      tile += sh.red[q];
+    }
+    const double prev = __shfl_up(iw, 1);
+    const double excl = carry + pre + (lane == 0 ? 0.0 : prev);
+    const double incl = carry + pre + iw;
+    if (sl < nslot && incl > thr && ts > 0.0) atomicMin(&sh.owner, tid);
+    __syncthreads();
+    if (tid == sh.owner) {
+      double cum = excl;
+      int tok = -1;
+      auto walk = [&](int v, float z, float d) {
+        const double x = pw(z, d);
+        cum += x;
+        if (tok < 0 && cum > thr) tok = v;
+      };
+      visit_ids<L>(tp, pw.resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), walk);
+      sh.ptok = tok >= 0 ? tok : tl;    // rounding: the last id with weight of this slot
+      sh.found = 1;
+    }
+    __syncthreads();
+    if (sh.found) break;
+    carry += tile;
+  }
+  if (!sh.found) {                      // w * total at or past the end: last id with weight
+    if (mylast >= 0) atomicMax(&sh.plast, mylast);
+    __syncthreads();
+    if (tid == 0) sh.ptok = sh.plast;
+  }
+  __syncthreads();
+  return sh.ptok;
+}
+
 
 // Correction or bonus draw of request b by one block of >= kBlock threads
 // (KEEP: see rescan_unit).
@@ -743,29 +938,50 @@ __device__ __forceinline__ void finalize_request(const Args& a, int b, const Req
       sh.Z = Z;
       sh.mode = mode;
       sh.fallback = fb;
+      sh.tok = -1;
+      sh.cert = 0;
     }
   }
   __syncthreads();
   const int mode = sh.mode;
   const Elem* tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
+  const Elem* dp = (R.kind == KIND_RESID)
+                       ? static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld : nullptr;
   int tok;
+  double fm = -1.0;
   if (mode == DRAW_RESID) {
-    const Elem* dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
     const int s0 = sh.unit * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
     tok = rescan_unit<L, PER_R, KEEP>(tp, dp, s0, s1, R.y, resid_weights(R, a), sh.before,
-                                      sh.thr, sh.fallback, sh.wave, &sh.owner);
+                                      sh.thr, sh.fallback, sh.wave, &sh.owner, &fm);
   } else {
     const int s0 = sh.unit * a.seg;
     const int s1 = min(s0 + a.seg, a.V);
     tok = rescan_unit<L, PER_S, KEEP>(tp, (const Elem*)nullptr, s0, s1, -1,
                                       target_weights(R, a), sh.before, sh.thr, sh.fallback,
-                                      sh.wave, &sh.owner);
+                                      sh.wave, &sh.owner, &fm);
   }
   if (tok != -2) {
-    a.out[R.trow] = tok;
-    if (a.resid_out)
-      a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? sh.Z : 0.0) : -1.f;
+    sh.tok = tok;
+    // a residual draw that fell back to p because its fp32 total was 0 is
+    // never certified: the exact total may be positive
+    sh.cert = (fm > kCertMargin && (R.kind != KIND_RESID || mode == DRAW_RESID)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (sh.cert) {
+    if (tid == 0) {
+      a.out[R.trow] = sh.tok;
+      if (a.resid_out)
+        a.resid_out[b] = (R.kind == KIND_RESID) ? (float)(mode == DRAW_RESID ? sh.Z : 0.0) : -1.f;
+    }
+    return;
+  }
+  double Z = 0.0;
+  const int ptok = precise_draw<L>(tp, dp, a.V, (double)R.Mp, (double)R.Mq, a.T64, w,
+                                   R.kind == KIND_RESID, &Z, sh);
+  if (tid == 0) {
+    a.out[R.trow] = ptok;
+    if (a.resid_out) a.resid_out[b] = (R.kind == KIND_RESID) ? (float)Z : -1.f;
   }
 }
 
@@ -1437,8 +1653,10 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.resid_out = sample ? resid_out : nullptr;
   if (sample) {
     set_scale((double)temperature, &a.c, &a.c64);
+    a.T64 = (double)temperature;
   } else {
     set_scale(1.0, &a.c, &a.c64);
+    a.T64 = 1.0;
   }
   a.ws.hdr = reinterpret_cast<Header*>(wb + z.off_hdr);
   a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);

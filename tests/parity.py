@@ -29,8 +29,18 @@ def run_hip(batch: synth.Batch, **kw) -> dict:
     return {k: (None if v is None else v.cpu().numpy()) for k, v in res.items()}
 
 
-def run_oracle(batch: synth.Batch) -> dict:
-    return oracle.verify_batch(**synth.as_numpy(batch))
+def run_oracle(batch: synth.Batch, chunk: int = 0) -> dict:
+    """The oracle on every request of the batch.  chunk > 0 runs it on
+    consecutive groups of that many requests (host copies of one group at a
+    time) and concatenates the results, which stay in the packed layout because
+    requests are independent and the groups keep their order."""
+    if chunk <= 0 or batch.B <= chunk:
+        return oracle.verify_batch(**synth.as_numpy(batch))
+    parts = []
+    for s0 in range(0, batch.B, chunk):
+        sub = synth.select_requests(batch, list(range(s0, min(s0 + chunk, batch.B))), device="cpu")
+        parts.append(oracle.verify_batch(**synth.as_numpy(sub)))
+    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
 
 
 def compare(batch: synth.Batch, got: dict, ref: dict, label: str = "") -> int:

@@ -161,7 +161,7 @@ def test_early_exit_repeat_and_stream():
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_early_exit_full_size(cfg):
     """Full workload shape in the launch configuration the benchmark times:
-    bit-identical to the all-rows path, and a seeded sample against the oracle."""
+    bit-identical to the all-rows path, and every request against the oracle."""
     _log(f"[early-exit full] cfg={cfg} generating")
     batch = synth.make_batch(cfg, DEV)
     torch.cuda.synchronize()
@@ -170,22 +170,9 @@ def test_early_exit_full_size(cfg):
     got = run_hip(batch, max_k=max_k)
     full = run_hip(batch)
     _assert_same_as_all_rows(batch, got, full, f"full cfg{cfg}")
-    rng = np.random.default_rng(2000 + cfg)
-    reqs = sorted(rng.choice(batch.B, size=min(12, batch.B), replace=False).tolist())
-    sub = synth.select_requests(batch, reqs, device="cpu")
-    ref = run_oracle(sub)
-    nd = batch.num_draft.astype(np.int64)
-    off = np.concatenate([[0], np.cumsum(nd)])
-    sel = {"accepted_len": got["accepted_len"][reqs]}
-    sel["out_tokens"] = np.concatenate(
-        [got["out_tokens"][off[b] + b: off[b] + b + nd[b] + 1] for b in reqs])
-    if got.get("p_draft") is not None:
-        dr = np.concatenate([np.arange(off[b], off[b] + nd[b]) for b in reqs]).astype(np.int64)
-        sel["p_draft"] = got["p_draft"][dr]
-        sel["q_draft"] = got["q_draft"][dr]
-        sel["resid_mass"] = got["resid_mass"][reqs]
-    near = compare(sub, sel, _oracle_as_tested(sub, sel, ref), f"early-exit full cfg{cfg}")
-    _log(f"[early-exit full] cfg={cfg}: sampled {len(reqs)}, near_ties={near}")
+    ref = run_oracle(batch, chunk=32)
+    near = compare(batch, got, _oracle_as_tested(batch, got, ref), f"early-exit full cfg{cfg}")
+    _log(f"[early-exit full] cfg={cfg}: {batch.B} requests, near_ties={near}")
 
 
 @pytest.mark.parametrize("extra", [0, 70])
