@@ -122,33 +122,78 @@ def host_cpu() -> str:
                     break
     except OSError:
         pass
-    return f"{model}, {os.cpu_count()} logical cores (the oracle used 1)"
+    return f"{model}, {os.cpu_count()} logical cores visible"
 
 
-def cpu_baseline(batch, min_seconds: float, max_requests: int):
-    """The oracle as it stands, on the first requests of the batch, until at
-    least `min_seconds` of CPU time have been spent (or `max_requests`)."""
+def host_threads() -> int:
+    """Host threads the oracle may use: the CPUs this process may run on, capped
+    by OMP_NUM_THREADS when it is set (the GPU host's share of its CPUs)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def oracle_inputs(batch, chunk: int = 16):
+    """Host copies of the batch in groups of `chunk` consecutive requests (the
+    layout the oracle takes), made before any oracle timing starts."""
     import synth
+    parts = []
+    for s0 in range(0, batch.B, chunk):
+        sub = synth.select_requests(batch, list(range(s0, min(s0 + chunk, batch.B))), device="cpu")
+        parts.append(synth.as_numpy(sub))
+    return parts
+
+
+def run_oracle_timed(parts, threads: int, early_exit: bool):
+    """The oracle as it stands on every group, serially or by a pool of threads
+    over the groups (requests are independent; NumPy releases the GIL inside
+    its array loops).  Returns (results concatenated in request order, seconds)."""
     import oracle
-    done_pos = 0
-    done_req = 0
-    rows = 0
-    t_total = 0.0
-    step = 16
-    while done_req < min(batch.B, max_requests) and t_total < min_seconds:
-        reqs = list(range(done_req, min(done_req + step, batch.B)))
-        sub = synth.select_requests(batch, reqs, device="cpu")
-        d = synth.as_numpy(sub)
-        t0 = time.perf_counter()
-        oracle.verify_batch(**d)
-        t_total += time.perf_counter() - t0
-        done_pos += int(sub.num_draft.sum())
-        rows += sub.K + sub.B + int(sub.num_draft[sub.greedy == 0].sum()) if sub.temperature else sub.K + sub.B
-        done_req += len(reqs)
-    return dict(value=done_pos / t_total if t_total > 0 else None, unit="verified draft positions/s",
-                cores=1, kind="oracle", host=host_cpu(),
-                sample=f"first {done_req} of {batch.B} requests ({done_pos} positions, {rows} logit rows), "
-                       f"{t_total:.1f} s of fp64 NumPy on one host core")
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(d):
+        return oracle.verify_batch(**d, early_exit=early_exit)
+
+    t0 = time.perf_counter()
+    if threads <= 1:
+        res = [one(d) for d in parts]
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            res = list(ex.map(one, parts))
+    dt = time.perf_counter() - t0
+    return {k: np.concatenate([r[k] for r in res]) for k in res[0]}, dt
+
+
+def parity_summary(batch, gpu: dict, ref: dict, near_tie: float = 1e-6) -> dict:
+    """GPU outputs against the oracle's, per request: equal (accepted length,
+    committed tokens), else a near-tie when the oracle's deciding margin is
+    below 1e-6 relative, else a mismatch.  Also the largest |p(y) - p_oracle|
+    and |q(y) - q_oracle| over the stochastic draft rows."""
+    nd = batch.num_draft.astype(np.int64)
+    off = np.concatenate([[0], np.cumsum(nd)])
+    mism = near = 0
+    for b in range(batch.B):
+        sl = slice(int(off[b]) + b, int(off[b]) + b + int(nd[b]) + 1)
+        if (int(gpu["accepted_len"][b]) == int(ref["accepted_len"][b])
+                and np.array_equal(gpu["out_tokens"][sl].astype(np.int64), ref["out_tokens"][sl])):
+            continue
+        if not batch.greedy[b] and batch.temperature is not None and ref["margin"][b] < near_tie:
+            near += 1
+        else:
+            mism += 1
+    res = {"requests": int(batch.B), "mismatches": mism, "near_ties": near}
+    if gpu.get("p_draft") is not None and batch.temperature is not None and batch.K > 0:
+        rows = np.repeat(batch.greedy == 0, nd)
+        if rows.any():
+            for name in ("p_draft", "q_draft"):
+                res[f"max_abs_err_{name[0]}"] = float(np.max(np.abs(
+                    gpu[name][rows].astype(np.float64) - ref[name][rows])))
+    return res
 
 
 def cpu_baseline_tree(tb, min_seconds: float):
@@ -397,7 +442,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle (CPU baseline and parity against it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the chosen workload (no `configs` object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup+steps calls and exit without the JSON report (for rocprofv3)")
@@ -444,202 +492,277 @@ def main():
         full = synth.CONFIGS[cfg_id]
         shard_kw = {"V": full["V"] // args.shards} if args.shard == "vocab" \
             else {"B": max(1, full["B"] // args.shards)}
-    batch = synth.make_batch(cfg_id, dev, **shard_kw)
-    torch.cuda.synchronize()
+    hip = HipEvents()
+    head = VerifyWorkload(synth.make_batch(cfg_id, dev, **shard_kw), sv, torch, hip, args.mall_flush)
+    if args.profile_only:
+        head.profile_only(args.early_exit, args.warmup, args.steps)
+        return
+    res = head.report(args, args.early_exit, args.steps, args.warmup)
+    if shard_kw:
+        res["config"]["parallelism"] = f"one GPU's share of a {args.shards}-way {args.shard} split"
 
-    # Pre-built call: every buffer resident in HBM before timing.
-    nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=dev)
-    gm = torch.as_tensor(batch.greedy, dtype=torch.uint8, device=dev) if batch.greedy.any() else None
-    acc = torch.empty(batch.B, dtype=torch.int32, device=dev)
-    out = torch.empty(batch.K + batch.B, dtype=torch.int32, device=dev)
-    pdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
-    qdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
-    rm = torch.empty(batch.B, dtype=torch.float32, device=dev)
-    ws_bytes = sv.spec_verify_workspace_bytes(batch.B, batch.K, batch.V)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    bt = sv.make_batch_struct(batch.target, batch.draft, batch.tokens, nd)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    lib = sv.lib()
-    greedy_only = batch.temperature is None
-    kmax = int(batch.num_draft.max()) if batch.K > 0 else 0
+    # the oracle: parity of the headline outputs and the CPU baseline
+    if not args.no_cpu_baseline:
+        parts = oracle_inputs(head.batch)
+        nthr = host_threads()
+        ref1, t1 = run_oracle_timed(parts, 1, False)
+        refn, tn = run_oracle_timed(parts, nthr, False)
+        _, te1 = run_oracle_timed(parts, 1, True)
+        _, ten = run_oracle_timed(parts, nthr, True)
+        assert all(np.array_equal(ref1[k], refn[k]) for k in ("accepted_len", "out_tokens"))
+        pos = head.batch.K
+        res["parity"] = parity_summary(head.batch, head.outputs(), ref1)
+        res["parity"]["rule"] = ("every request of the timed batch against the fp64 oracle; a "
+                                 "near-tie is a disagreement whose deciding margin is below 1e-6 "
+                                 "relative")
+        res["cpu_baseline"] = {
+            "value": pos / tn, "unit": "verified draft positions/s", "cores": nthr,
+            "kind": "oracle", "host": host_cpu(),
+            "sample": (f"all {head.batch.B} requests ({pos} positions) of the timed batch, fp64 "
+                       f"NumPy oracle, {nthr} threads over groups of 16 requests, all rows"),
+            "variants": {
+                "all_rows_1_thread": {"value": pos / t1, "seconds": t1},
+                f"all_rows_{nthr}_threads": {"value": pos / tn, "seconds": tn},
+                "early_exit_1_thread": {"value": pos / te1, "seconds": te1},
+                f"early_exit_{nthr}_threads": {"value": pos / ten, "seconds": ten},
+            },
+        }
+        del parts
 
-    def make_call(early_exit: bool):
-        if greedy_only:
+    # every workload, briefly (the headline's own entry reuses its numbers)
+    if not args.no_configs and not shard_kw:
+        configs = {}
+        for cid in sorted(synth.CONFIGS):
+            if cid == cfg_id:
+                wl = head
+                entry = wl.summary(res)
+            else:
+                wl = VerifyWorkload(synth.make_batch(cid, dev), sv, torch, hip, args.mall_flush)
+                r = wl.report(args, False, min(args.steps, 50), min(args.warmup, 10),
+                              with_other=True, acceptance=False)
+                entry = wl.summary(r)
+            if not args.no_cpu_baseline:
+                if cid == cfg_id:
+                    entry["parity"] = res["parity"]
+                else:
+                    ref, _ = run_oracle_timed(oracle_inputs(wl.batch), host_threads(), False)
+                    entry["parity"] = parity_summary(wl.batch, wl.outputs(), ref)
+            configs[wl.batch.name] = entry
+            if wl is not head:
+                wl.release()
+        res["configs"] = configs
+    print(json.dumps(res), flush=True)
+
+
+class VerifyWorkload:
+    """One resident verification batch with pre-built C-ABI calls."""
+
+    def __init__(self, batch, sv, torch, hip, mall_flush):
+        self.batch, self.sv, self.torch, self.hip = batch, sv, torch, hip
+        dev = batch.target.device
+        torch.cuda.synchronize()
+        self.nd = torch.as_tensor(batch.num_draft, dtype=torch.int32, device=dev)
+        self.gm = (torch.as_tensor(batch.greedy, dtype=torch.uint8, device=dev)
+                   if batch.greedy.any() else None)
+        self.acc = torch.empty(batch.B, dtype=torch.int32, device=dev)
+        self.out = torch.empty(batch.K + batch.B, dtype=torch.int32, device=dev)
+        self.pdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
+        self.qdr = torch.empty(max(batch.K, 1), dtype=torch.float32, device=dev)
+        self.rm = torch.empty(batch.B, dtype=torch.float32, device=dev)
+        self.ws_bytes = sv.spec_verify_workspace_bytes(batch.B, batch.K, batch.V)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.bt = sv.make_batch_struct(batch.target, batch.draft, batch.tokens, self.nd)
+        self.sh = torch.cuda.current_stream().cuda_stream
+        self.greedy_only = batch.temperature is None
+        self.kmax = int(batch.num_draft.max()) if batch.K > 0 else 0
+        self.es = 4 if batch.dtype == "f32" else 2
+        self.k_np = batch.num_draft.astype(np.int64)
+        self.stoch = np.zeros(batch.B, bool) if self.greedy_only else (batch.greedy == 0)
+        self.bytes_all = self.rows_read(False) * batch.V * self.es
+        self.flush = mall_flush == "on" or (mall_flush == "auto" and self.bytes_all < (768 << 20))
+        self.scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if self.flush else None
+
+    def call(self, early_exit: bool):
+        lib, bt, ws, wsb, sh = self.sv.lib(), self.bt, self.ws, self.ws_bytes, self.sh
+        acc, out = self.acc.data_ptr(), self.out.data_ptr()
+        if self.greedy_only:
             if early_exit:
                 return lambda: lib.spec_verify_greedy_early_exit(
-                    ctypes.byref(bt), kmax, acc.data_ptr(), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
-            return lambda: lib.spec_verify_greedy(ctypes.byref(bt), acc.data_ptr(), out.data_ptr(),
-                                                  ws.data_ptr(), ws_bytes, sh)
-        T = ctypes.c_float(batch.temperature)
-        a_ptrs = (gm.data_ptr() if gm is not None else None, batch.u_accept.data_ptr(),
-                  batch.u_final.data_ptr(), acc.data_ptr(), out.data_ptr(), pdr.data_ptr(),
-                  qdr.data_ptr(), rm.data_ptr())
+                    ctypes.byref(bt), self.kmax, acc, out, ws.data_ptr(), wsb, sh)
+            return lambda: lib.spec_verify_greedy(ctypes.byref(bt), acc, out, ws.data_ptr(), wsb, sh)
+        T = ctypes.c_float(self.batch.temperature)
+        a_ptrs = (self.gm.data_ptr() if self.gm is not None else None,
+                  self.batch.u_accept.data_ptr(), self.batch.u_final.data_ptr(), acc, out,
+                  self.pdr.data_ptr(), self.qdr.data_ptr(), self.rm.data_ptr())
         if early_exit:
-            return lambda: lib.spec_verify_sample_early_exit(ctypes.byref(bt), kmax, T, *a_ptrs,
-                                                             ws.data_ptr(), ws_bytes, sh)
-        return lambda: lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), ws_bytes, sh)
+            return lambda: lib.spec_verify_sample_early_exit(ctypes.byref(bt), self.kmax, T,
+                                                             *a_ptrs, ws.data_ptr(), wsb, sh)
+        return lambda: lib.spec_verify_sample(ctypes.byref(bt), T, *a_ptrs, ws.data_ptr(), wsb, sh)
 
-    ee = args.early_exit
-    call = make_call(ee)
-    for _ in range(args.warmup):
-        assert call() == 0
-    torch.cuda.synchronize()
-    if args.profile_only:
-        for _ in range(args.steps):
-            assert call() == 0
-        torch.cuda.synchronize()
-        print(f"profile-only: {args.warmup + args.steps} calls of {batch.name}", flush=True)
-        return
-
-    hip = HipEvents()
-    es = 4 if batch.dtype == "f32" else 2
-    k_np = batch.num_draft.astype(np.int64)
-    stoch = np.zeros(batch.B, bool) if greedy_only else (batch.greedy == 0)
-
-    def rows_read(early_exit: bool) -> int:
+    def rows_read(self, early_exit: bool) -> int:
+        b = self.batch
         if not early_exit:      # every target row, the draft rows of stochastic requests
-            return batch.K + batch.B + int(k_np[stoch].sum())
-        # every row of the position windows up to the one holding each cut
-        a_np = acc.cpu().numpy().astype(np.int64)
-        return early_exit_rows_read(a_np, k_np, stoch, kmax)
+            return b.K + b.B + int(self.k_np[self.stoch].sum())
+        a_np = self.acc.cpu().numpy().astype(np.int64)
+        return early_exit_rows_read(a_np, self.k_np, self.stoch, self.kmax)
 
-    bytes_all = rows_read(False) * batch.V * es
-    flush = args.mall_flush == "on" or (args.mall_flush == "auto" and bytes_all < (768 << 20))
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+    def profile_only(self, early_exit, warmup, steps):
+        fn = self.call(early_exit)
+        for _ in range(warmup + steps):
+            assert fn() == 0
+        self.torch.cuda.synchronize()
+        print(f"profile-only: {warmup + steps} calls of {self.batch.name}", flush=True)
 
-    def timed(fn, steps):
-        """Per call: GPU time from HIP events around the C-ABI call on its stream
-        (median, p10, p90), and the mean of the interval the library records
-        around its row-statistics launches; plus wall time per call.  With the
-        MALL flush a 512 MiB fill runs between calls, outside the call events."""
-        ev_b, ev_e = hip.create(steps), hip.create(steps)
+    def timed(self, fn, steps):
+        """Wall clock over `steps` back-to-back calls with nothing else on the
+        stream (a 512 MiB fill between calls when the MALL is flushed); then,
+        in separate passes of up to 50 calls, the GPU time of each call from
+        HIP events around it on its stream, and the duration of the
+        row-statistics launch from the events the library records around it."""
+        torch, hip, sh = self.torch, self.hip, self.sh
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            if flush:
-                scratch.zero_()
-            sv.spec_verify_set_profile_events(ev_b[i], ev_e[i])
+        for _ in range(steps):
+            if self.flush:
+                self.scratch.zero_()
             fn()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        sv.spec_verify_set_profile_events(None, None)
-        ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
-        hip.destroy(ev_b + ev_e)
-        wall = (t1 - t0) / steps
-        # per-call GPU time in a separate pass (events around each call would
-        # slow the back-to-back loop above)
+        wall = (time.perf_counter() - t0) / steps
         n = min(steps, 50)
         cb, ce = hip.create(n), hip.create(n)
         for i in range(n):
-            if flush:
-                scratch.zero_()
+            if self.flush:
+                self.scratch.zero_()
             hip.record(cb[i], sh)
             fn()
             hip.record(ce[i], sh)
         torch.cuda.synchronize()
         call_ms = np.array([hip.elapsed_ms(cb[i], ce[i]) for i in range(n)])
         hip.destroy(cb + ce)
-        step = float(np.median(call_ms)) / 1e3 if flush else wall
-        return step, float(np.mean(ms)) / 1e3, call_ms, wall
+        eb, ee = hip.create(n), hip.create(n)
+        for i in range(n):
+            if self.flush:
+                self.scratch.zero_()
+            self.sv.spec_verify_set_profile_events(eb[i], ee[i])
+            fn()
+        torch.cuda.synchronize()
+        self.sv.spec_verify_set_profile_events(None, None)
+        stats_ms = [hip.elapsed_ms(eb[i], ee[i]) for i in range(n)]
+        hip.destroy(eb + ee)
+        step = float(np.median(call_ms)) / 1e3 if self.flush else wall
+        return step, float(np.mean(stats_ms)) / 1e3, call_ms, wall
 
-    step_s, t_stats, call_ms, wall_s = timed(call, args.steps)
-    positions = int(batch.num_draft.sum())
-    rows = rows_read(ee)
-    bytes_stats = rows * batch.V * es
-    achieved = bytes_stats / t_stats / 1e9
+    def report(self, args, ee, steps, warmup, with_other=True, acceptance=True) -> dict:
+        b = self.batch
+        fn = self.call(ee)
+        for _ in range(warmup):
+            assert fn() == 0
+        step_s, t_stats, call_ms, wall_s = self.timed(fn, steps)
+        positions = int(b.num_draft.sum())
+        bytes_stats = self.rows_read(ee) * b.V * self.es
+        achieved = bytes_stats / t_stats / 1e9
+        path = lambda e: ("early exit (max_k = %d)" % self.kmax) if e else "all rows"
+        res = {
+            "metric": METRIC, "value": positions / step_s, "unit": "verified draft positions/s",
+            "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": step_s * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {
+                "workload": b.name, "B": b.B, "K": b.K, "V": b.V, "logits": b.dtype,
+                "temperature": b.temperature,
+                "requests": ("greedy" if self.greedy_only else
+                             f"{int((b.greedy == 1).sum())} greedy, {int((b.greedy == 0).sum())} stochastic"),
+                "parallelism": "single GPU", "path": path(ee), "launch_plan": args.launch_plan,
+            },
+            "call_gpu_us": {"median": float(np.median(call_ms)) * 1e3,
+                            "p10": float(np.percentile(call_ms, 10)) * 1e3,
+                            "p90": float(np.percentile(call_ms, 90)) * 1e3,
+                            "wall_per_call": wall_s * 1e6,
+                            "timing": ("median of per-call HIP events, 512 MiB MALL flush between calls"
+                                       if self.flush else "wall clock over back-to-back calls")},
+            "rows_per_s": (b.K + b.B) / step_s,
+            "hbm_gbs_step": self.bytes_all / step_s / 1e9 if not ee else bytes_stats / step_s / 1e9,
+            "hbm_frac_step": (self.bytes_all if not ee else bytes_stats) / step_s / 1e9 / PEAK_HBM_GBS,
+            "roofline": {
+                "kernel": ("rounds: k_round + k_decide_round per window" if ee
+                           else "k_stats (row statistics)"),
+                "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": self.traffic(ee),
+                "algorithmic_bytes_per_launch": bytes_stats, "avg_kernel_ms": t_stats * 1e3,
+            },
+        }
+        tr = res["roofline"]["traffic"]
+        res["roofline"]["traffic_ratio"] = (tr / bytes_stats) if tr else None
+        if with_other:
+            other = self.call(not ee)
+            for _ in range(max(warmup // 2, 2)):
+                assert other() == 0
+            o_step, o_t, _, _ = self.timed(other, max(steps // 2, 5))
+            o_bytes = self.rows_read(not ee) * b.V * self.es
+            res["other_path"] = {
+                "path": path(not ee), "value": positions / o_step, "ms_per_step": o_step * 1e3,
+                "logit_bytes_read": o_bytes, "hbm_gbs_step": o_bytes / o_step / 1e9,
+                "timed_interval_ms": o_t * 1e3, "speedup_of_headline": o_step / step_s,
+            }
+        assert fn() == 0            # leave the headline path's outputs in the buffers
+        self.torch.cuda.synchronize()
+        if acceptance:
+            res["acceptance"] = self.acceptance()
+        return res
 
-    # the other entry point on the same batch, for comparison
-    other = make_call(not ee)
-    for _ in range(max(args.warmup // 2, 2)):
-        assert other() == 0
-    o_step, o_t, _, _ = timed(other, max(args.steps // 2, 5))
-    o_bytes = rows_read(not ee) * batch.V * es
-    call()                      # leave the headline path's outputs in acc/out
-    torch.cuda.synchronize()
-
-    traffic = None
-    if os.path.exists(TRAFFIC):
+    def traffic(self, ee):
+        if not os.path.exists(TRAFFIC):
+            return None
         with open(TRAFFIC) as f:
             tr = json.load(f)
-        entry = tr.get(batch.name if not ee else batch.name + "/early_exit")
+        entry = tr.get(self.batch.name if not ee else self.batch.name + "/early_exit")
         if entry and entry.get("source_hash") == kernel_source_hash():
-            traffic = entry.get("hbm_bytes_per_launch")
+            return entry.get("hbm_bytes_per_launch")
+        return None
 
-    path = lambda e: ("early exit (max_k = %d)" % kmax) if e else "all rows"
-    res = {
-        "metric": METRIC,
-        "value": positions / step_s,
-        "unit": "verified draft positions/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": batch.name, "B": batch.B, "K": batch.K, "V": batch.V,
-            "logits": batch.dtype, "temperature": batch.temperature,
-            "requests": ("greedy" if greedy_only else
-                         f"{int((batch.greedy == 1).sum())} greedy, {int((batch.greedy == 0).sum())} stochastic"),
-            "parallelism": ("single GPU" if not shard_kw else
-                            f"one GPU's share of a {args.shards}-way {args.shard} split"),
-            "path": path(ee),
-            "launch_plan": args.launch_plan,
-        },
-        "call_gpu_us": {"median": float(np.median(call_ms)) * 1e3,
-                        "p10": float(np.percentile(call_ms, 10)) * 1e3,
-                        "p90": float(np.percentile(call_ms, 90)) * 1e3,
-                        "wall_per_call": wall_s * 1e6,
-                        "timing": ("median of per-call HIP events, 512 MiB MALL flush between calls"
-                                   if flush else "wall clock over back-to-back calls")},
-        "rows_per_s": (batch.K + batch.B) / step_s,
-        "hbm_gbs_step": bytes_stats / step_s / 1e9,
-        "hbm_frac_step": bytes_stats / step_s / 1e9 / PEAK_HBM_GBS,
-        "roofline": {
-            "kernel": ("rounds: k_round + k_decide_round per position" if ee
-                       else "k_stats (row statistics)"),
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic,
-            "traffic_ratio": (traffic / bytes_stats) if traffic else None,
-            "algorithmic_bytes_per_launch": bytes_stats,
-            "avg_kernel_ms": t_stats * 1e3,
-        },
-        "other_path": {
-            "path": path(not ee),
-            "value": positions / o_step,
-            "ms_per_step": o_step * 1e3,
-            "logit_bytes_read": o_bytes,
-            "hbm_gbs_step": o_bytes / o_step / 1e9,
-            "timed_interval_ms": o_t * 1e3,
-            "speedup_of_headline": o_step / step_s,
-        },
-    }
-    st_out = torch.empty(4 + max(kmax, 1), dtype=torch.float64, device=dev)
-    sv.spec_verify_accept_stats(acc, nd, max(kmax, 1), out=st_out)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(50):
-        sv.spec_verify_accept_stats(acc, nd, max(kmax, 1), out=st_out)
-    e1.record()
-    torch.cuda.synchronize()
-    st = st_out.cpu().numpy()
-    res["acceptance"] = {
-        "note": "from the timed calls' outputs; MAL counts the correction/bonus token, AR = kept/proposed drafts",
-        "mean_kept_drafts": float(st[1]), "MAL": float(st[2]), "AR": float(st[3]),
-        "per_position": [round(float(x), 4) for x in st[4:4 + max(kmax, 1)]],
-        "stats_call_us": e0.elapsed_time(e1) * 1e3 / 50,
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(batch, args.cpu_seconds, max_requests=batch.B)
-    print(json.dumps(res), flush=True)
+    def acceptance(self) -> dict:
+        torch, sv = self.torch, self.sv
+        kmax = max(self.kmax, 1)
+        st_out = torch.empty(4 + kmax, dtype=torch.float64, device=self.acc.device)
+        sv.spec_verify_accept_stats(self.acc, self.nd, kmax, out=st_out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            sv.spec_verify_accept_stats(self.acc, self.nd, kmax, out=st_out)
+        e1.record()
+        torch.cuda.synchronize()
+        st = st_out.cpu().numpy()
+        return {
+            "note": "from the timed calls' outputs; MAL counts the correction/bonus token, AR = kept/proposed drafts",
+            "mean_kept_drafts": float(st[1]), "MAL": float(st[2]), "AR": float(st[3]),
+            "per_position": [round(float(x), 4) for x in st[4:4 + kmax]],
+            "stats_call_us": e0.elapsed_time(e1) * 1e3 / 50,
+        }
+
+    def outputs(self) -> dict:
+        o = {"accepted_len": self.acc.cpu().numpy(), "out_tokens": self.out.cpu().numpy()}
+        if not self.greedy_only:
+            o.update(p_draft=self.pdr[:self.batch.K].cpu().numpy(),
+                     q_draft=self.qdr[:self.batch.K].cpu().numpy(), resid_mass=self.rm.cpu().numpy())
+        return o
+
+    def summary(self, r: dict) -> dict:
+        """The per-workload line of the `configs` object."""
+        out = {
+            "B": self.batch.B, "K": self.batch.K, "V": self.batch.V, "logits": self.batch.dtype,
+            "step_us": r["ms_per_step"] * 1e3, "timing": r["call_gpu_us"]["timing"],
+            "positions_per_s": r["value"], "bytes_all": self.bytes_all,
+            "call_frac_of_8TBs": r["hbm_frac_step"],
+            "k_stats_frac_of_8TBs": r["roofline"]["frac"], "k_stats_us": r["roofline"]["avg_kernel_ms"] * 1e3,
+        }
+        if "other_path" in r:
+            out["early_exit_step_us"] = r["other_path"]["ms_per_step"] * 1e3
+            out["early_exit_positions_per_s"] = r["other_path"]["value"]
+        return out
+
+    def release(self):
+        self.batch = self.scratch = self.ws = None
+        self.torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

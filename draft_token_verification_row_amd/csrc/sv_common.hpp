@@ -41,6 +41,9 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 #ifndef SV_SEG_BYTES
 #define SV_SEG_BYTES 32768
 #endif
+#ifndef SV_MALL_ORDER
+#define SV_MALL_ORDER 1
+#endif
 constexpr int kUnroll = SV_UNROLL;       // 16-byte chunks per lane per step of a unit loop
 #ifndef SV_ARGMAX_UNROLL
 #define SV_ARGMAX_UNROLL 4
@@ -102,13 +105,15 @@ struct Header {
   int n_rows3[3];     // early-exit rounds: rows listed for a round (three lists in rotation)
   int n_res3[3];      // early-exit rounds: residual sweeps listed for a round
   int n_alive3[3];    // early-exit rounds: requests deciding a position in the round
-  int pad[51];
+  int n_rows_b;       // rows of the second row list (streamed last)
+  int pad[50];
 };
 
 struct Workspace {
   Header* hdr;
   ReqInfo* req;
   uint32_t* rowdesc;   // [2K + B]
+  uint32_t* rowdesc_b; // [2B]  rows streamed last (position-0 pairs of stochastic requests)
   int* resid_list;     // [B]
   Partial* pt;         // [(K + B) * nseg]
   Partial* pd;         // [K * nseg]
@@ -140,6 +145,8 @@ struct Args {
   double T64;         // the fp32 temperature, widened (the fp64 draw divides by it)
   const uint32_t* rowlist;   // rows k_stats reads (all rows, or one round's)
   const int* rowcount;       // number of rows in rowlist
+  const uint32_t* rowlist_b = nullptr;   // rows k_stats reads after those, or NULL
+  const int* rowcount_b = nullptr;       // number of rows in rowlist_b (when not NULL)
   int ee_round;              // early-exit round, -1 on the all-rows path
   int ee_lo, ee_hi, ee_nhi;  // early exit: positions [lo, hi) decided in this round, [hi, nhi) in the next
   int max_k;                 // early-exit: bound on every num_draft[b] (trees: on every depth)
@@ -433,23 +440,28 @@ __device__ __forceinline__ Scan2 block_scan2(long long v0, long long v1, long lo
 }
 
 // ------------------------------------------------------------------ k_stats
-// Persistent grid; wavefront gw takes units gw, gw + W, ...  The descriptor of
-// the next unit is fetched while the current one streams.
+// Persistent grid; wavefront gw takes units gw, gw + W, ...  The rows come
+// from two lists, rowlist (rowcount entries) then rowlist_b (rowcount_b
+// entries, may be absent), in that order.  The descriptor of the next unit is
+// fetched while the current one streams.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
   using Elem = typename L::Elem;
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
-  const int n_units = *a.rowcount * a.nseg;
+  const int nA = *a.rowcount;
+  const int nB = a.rowcount_b ? *a.rowcount_b : 0;
+  const int n_units = (nA + nB) * a.nseg;
+  auto desc_of = [&](int ri) { return ri < nA ? a.rowlist[ri] : a.rowlist_b[ri - nA]; };
   const Elem* tgt = static_cast<const Elem*>(a.target);
   const Elem* drf = static_cast<const Elem*>(a.draft);
-  uint32_t next = (gw < n_units) ? a.rowlist[gw / a.nseg] : 0u;
+  uint32_t next = (gw < n_units) ? desc_of(gw / a.nseg) : 0u;
   for (int u = gw; u < n_units; u += W) {
     const uint32_t desc = next;
     const int ri = u / a.nseg;
     const int seg = u - ri * a.nseg;
-    if (u + W < n_units) next = a.rowlist[(u + W) / a.nseg];
+    if (u + W < n_units) next = desc_of((u + W) / a.nseg);
     const int row = (int)(desc & kRowMask);
     const bool is_draft = (desc & kDraftBit) != 0;
     const bool greedy = (desc & kGreedyBit) != 0;

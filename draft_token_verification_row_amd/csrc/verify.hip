@@ -48,19 +48,27 @@ namespace {
 
 // ------------------------------------------------------------------ k_plan
 
-// One workgroup: exclusive scans of k_b (all requests) and of k_b over
-// stochastic requests, 1024 requests per pass (wave shuffles + one LDS step).
+// One workgroup: exclusive scan of k_b -> request offsets and records, and
+// the two lists of rows k_stats streams, 1024 requests per pass (wave
+// shuffles + one LDS step).  The second list holds the position-0 (target,
+// draft) pair of every stochastic request with k_b >= 1; k_stats reads it
+// last.  About half of all cuts fall at position 0, and the residual sweep
+// re-reads exactly the rejected pair, so reading those pairs last leaves the
+// most likely re-reads in the last-level cache (MALL) when the sweep runs.
+// The first list holds every other row: all target rows of greedy requests,
+// target rows 1..k_b and draft rows 1..k_b-1 of stochastic requests (target
+// row 0 when k_b = 0).
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
-  __shared__ long long s_wk[kPlanWaves];
-  __shared__ long long s_ws[kPlanWaves];
+  __shared__ long long s_w0[kPlanWaves];
+  __shared__ long long s_w1[kPlanWaves];
   __shared__ long long s_tot[2];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
   const long long TB = (long long)a.K + a.B;
-  long long carry_k = 0, carry_s = 0;
+  long long carry_k = 0, carry_a = 0, carry_b = 0;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
     long long k = 0;
@@ -74,11 +82,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       k = kk;
       g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
     }
-    const long long ks = g ? 0 : k;
-    const Scan2 sc = block_scan2(k, ks, s_wk, s_ws, s_tot);
+    const bool pair0 = SV_MALL_ORDER && b < a.B && !g && k >= 1;
+    const long long cA = b >= a.B ? 0 : (g ? k + 1 : (pair0 ? 2 * k - 1 : 2 * k + 1));
+    const long long cB = pair0 ? 2 : 0;
+    const Scan2 sc = block_scan2(k, cA, s_w0, s_w1, s_tot);
+    __syncthreads();
+    const Scan2 sb = block_scan2(cB, 0, s_w0, s_w1, s_tot);
     const long long off = carry_k + sc.ex0;
-    const long long soff = carry_s + sc.ex1;
-    const long long tot_k = sc.tot0, tot_s = sc.tot1;
+    const long long aoff = carry_a + sc.ex1;
+    const long long boff = carry_b + sb.ex0;
     if (b < a.B) {
       ReqInfo r;
       r.off = (int)off;
@@ -93,28 +105,31 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       r.pad0 = r.pad1 = 0;
       r.Sp = r.Sq = 0.0;
       a.ws.req[b] = r;
-      for (long long i = 0; i <= k; ++i) {
-        const long long row = off + b + i;
-        if (row < TB) a.ws.rowdesc[row] = (uint32_t)row | (g ? kGreedyBit : 0u);
-      }
-      if (!g) {
-        for (long long i = 0; i < k; ++i) {
-          const long long slot = TB + soff + i;
-          if (slot < TB + a.K) a.ws.rowdesc[slot] = (uint32_t)(off + i) | kDraftBit;
-        }
+      const long long cap_a = 2ll * a.K + a.B;      // bounds: off may be wrong if num_draft is
+      const uint32_t gbit = g ? kGreedyBit : 0u;
+      long long j = aoff;
+      for (long long i = pair0 ? 1 : 0; i <= k; ++i, ++j)       // target rows
+        if (j < cap_a && off + b + i < TB) a.ws.rowdesc[j] = (uint32_t)(off + b + i) | gbit;
+      if (!g)
+        for (long long i = pair0 ? 1 : 0; i < k; ++i, ++j)      // draft rows
+          if (j < cap_a && off + i < a.K) a.ws.rowdesc[j] = (uint32_t)(off + i) | kDraftBit;
+      if (pair0 && boff + 1 < 2ll * a.B && off + b < TB && off < a.K) {
+        a.ws.rowdesc_b[boff] = (uint32_t)(off + b);
+        a.ws.rowdesc_b[boff + 1] = (uint32_t)off | kDraftBit;
       }
     }
-    carry_k += tot_k;
-    carry_s += tot_s;
+    carry_k += sc.tot0;
+    carry_a += sc.tot1;
+    carry_b += sb.tot0;
     __syncthreads();
   }
   if (tid == 0) {
     const bool bad = s_bad != 0 || carry_k != a.K;
-    const long long nrows = bad ? 0 : TB + carry_s;
     Header* h = a.ws.hdr;
     h->error = bad ? 1 : 0;
-    h->n_rows = (int)nrows;
-    h->n_units = (int)(nrows * a.nseg);
+    h->n_rows = bad ? 0 : (int)carry_a;
+    h->n_rows_b = bad ? 0 : (int)carry_b;
+    h->n_units = 0;
     h->n_resid = 0;
   }
 }
@@ -375,14 +390,17 @@ __global__ __launch_bounds__(kBlock) void k_decide(Args a) {
 
 // ------------------------------------------------------------------ draw weights
 // Residual weight [p - q]_+ and target weight p of one id, from the exact row
-// maxima and fp32 reciprocals of the row sums.  k_resid and k_finalize use
-// these same functions, so both see identical per-id values.
+// maxima and the row sums.  The residual sweep accumulates raw() =
+// S_p [p - q]_+ = [exp2((z - M_p) c) - rho exp2((d - M_q) c)]_+ with
+// rho = fl(S_p / S_q) and applies 1/S_p once per unit in fp64; single ids
+// (the rescan of one unit) use raw() times fl(1/S_p).
 struct ResidW {
-  float Mp, Mq, ip, iq, c;
-  __device__ __forceinline__ float operator()(float z, float d) const {
-    const float p = scaled_exp(z - Mp, c) * ip;
-    return fmaxf(fmaf(-scaled_exp(d - Mq, c), iq, p), 0.f);
+  float Mp, Mq, rho, ip, c;
+  double ip64;
+  __device__ __forceinline__ float raw(float z, float d) const {
+    return fmaxf(fmaf(-scaled_exp(d - Mq, c), rho, scaled_exp(z - Mp, c)), 0.f);
   }
+  __device__ __forceinline__ float operator()(float z, float d) const { return raw(z, d) * ip; }
 };
 
 struct TargetW {
@@ -396,8 +414,9 @@ __device__ __forceinline__ ResidW resid_weights(const ReqInfo& R, const Args& a)
   ResidW w;
   w.Mp = R.Mp;
   w.Mq = R.Mq;
-  w.ip = (float)(1.0 / R.Sp);
-  w.iq = (float)(1.0 / R.Sq);
+  w.rho = (float)(R.Sp / R.Sq);
+  w.ip64 = 1.0 / R.Sp;
+  w.ip = (float)w.ip64;
   w.c = a.c;
   return w;
 }
@@ -411,74 +430,96 @@ __device__ __forceinline__ TargetW target_weights(const ReqInfo& R, const Args& 
 }
 
 // Sum of [p - q]_+ over the ids [s0, s1) of one (target, draft) row pair, the
-// rejected id y excluded; one wavefront, result in every lane.
+// rejected id y excluded; one wavefront, result in every lane.  Lane l takes
+// the 16-byte chunks l, l + 64, ... in order; the loop is software-pipelined
+// over two register sets (the U chunks of both rows for the next step are
+// requested before the current ones are consumed, with no copies between the
+// sets), so any U gives the same sums bit for bit.
 template <class L, int U>
 __device__ __forceinline__ double resid_unit(const typename L::Elem* tp, const typename L::Elem* dp,
                                              const ResidW& fw, int y, int s0, int s1, int lane) {
   constexpr int E = L::E;
+  using Raw = typename L::Raw;
   const int n = s1 - s0;
   const int nchunk = n / E;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  auto chunk = [&](const typename L::Raw& rt, const typename L::Raw& rd, int id0) {
-    float vt[E], vd[E];
-    L::unpack(rt, vt);
-    L::unpack(rd, vd);
-    float r[E];
+  auto consume = [&](const Raw* rt, const Raw* rd) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) r[e] = fw(vt[e], vd[e]);
-    if ((unsigned)(y - id0) < (unsigned)E) {
+    for (int jj = 0; jj < U; ++jj) {
+      float vt[E], vd[E];
+      L::unpack(rt[jj], vt);
+      L::unpack(rd[jj], vd);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (id0 + e == y) r[e] = 0.f;   // reject => p(y) < q(y) => [p - q]_+ is 0 at y
+      for (int e = 0; e < E; ++e) acc[e] += fw.raw(vt[e], vd[e]);
     }
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += r[e];
   };
-  // software-pipelined as for_unit: the next U chunks of both rows are
-  // requested before the current ones are consumed
+  auto load = [&](Raw* rt, Raw* rd, int c0) {
+#pragma unroll
+    for (int jj = 0; jj < U; ++jj) {
+      rt[jj] = L::stream(tp + s0 + (size_t)(c0 + jj * kWave) * E);
+      rd[jj] = L::stream(dp + s0 + (size_t)(c0 + jj * kWave) * E);
+    }
+  };
   constexpr int per_it = kWave * U;
   const int nit = nchunk / per_it;
   int c = lane;
   if (nit > 0) {
-    typename L::Raw rt[U], rd[U];
-#pragma unroll
-    for (int jj = 0; jj < U; ++jj) {
-      rt[jj] = L::stream(tp + s0 + (size_t)(c + jj * kWave) * E);
-      rd[jj] = L::stream(dp + s0 + (size_t)(c + jj * kWave) * E);
-    }
-    for (int it = 1; it < nit; ++it) {
-      typename L::Raw nt[U], nd[U];
-#pragma unroll
-      for (int jj = 0; jj < U; ++jj) {
-        nt[jj] = L::stream(tp + s0 + (size_t)(c + per_it + jj * kWave) * E);
-        nd[jj] = L::stream(dp + s0 + (size_t)(c + per_it + jj * kWave) * E);
-      }
-#pragma unroll
-      for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
-#pragma unroll
-      for (int jj = 0; jj < U; ++jj) {
-        rt[jj] = nt[jj];
-        rd[jj] = nd[jj];
-      }
+    Raw at[U], ad[U], bt[U], bd[U];
+    load(at, ad, c);
+    int it = 1;
+    for (; it + 1 < nit; it += 2) {
+      load(bt, bd, c + per_it);
+      consume(at, ad);
+      c += per_it;
+      load(at, ad, c + per_it);
+      consume(bt, bd);
       c += per_it;
     }
-#pragma unroll
-    for (int jj = 0; jj < U; ++jj) chunk(rt[jj], rd[jj], s0 + (c + jj * kWave) * E);
+    if (it < nit) {
+      load(bt, bd, c + per_it);
+      consume(at, ad);
+      c += per_it;
+      consume(bt, bd);
+    } else {
+      consume(at, ad);
+    }
     c += per_it;
   }
-  for (; c < nchunk; c += kWave)
-    chunk(L::stream(tp + s0 + (size_t)c * E), L::stream(dp + s0 + (size_t)c * E), s0 + c * E);
+  for (; c < nchunk; c += kWave) {
+    Raw rt = L::stream(tp + s0 + (size_t)c * E), rd = L::stream(dp + s0 + (size_t)c * E);
+    float vt[E], vd[E];
+    L::unpack(rt, vt);
+    L::unpack(rd, vd);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += fw.raw(vt[e], vd[e]);
+  }
   const int tail0 = nchunk * E;
   if (lane < n - tail0) {
     const int v = s0 + tail0 + lane;
-    if (v != y) acc[0] += fw(L::one(tp + v), L::one(dp + v));
+    acc[0] += fw.raw(L::one(tp + v), L::one(dp + v));
+  }
+  // The rejected id y carries no residual weight (rejection means p(y) < q(y),
+  // so [p - q]_+ is 0 there), but its fp32 weight can round above 0: the lane
+  // that accumulated it takes the same value back out (y is the same in every
+  // lane, so the loop above has no per-id test).
+  if (y >= s0 && y < s1) {
+    const int rel = y - s0;
+    const bool chunked = rel < tail0;
+    const int owner = chunked ? (rel / E) & (kWave - 1) : rel - tail0;
+    const int slot = chunked ? rel % E : 0;
+    if (lane == owner) {
+      const float ry = fw.raw(L::one(tp + y), L::one(dp + y));
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e == slot) acc[e] -= ry;
+    }
   }
   float sl = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) sl += acc[e];
-  return wave_sum((double)sl);
+  return wave_sum((double)sl) * fw.ip64;
 }
 
 // ------------------------------------------------------------------ k_resid
@@ -488,9 +529,9 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
   using Elem = typename L::Elem;
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int W = gridDim.x * kWavesPerBlock;
   // each wavefront takes a contiguous range of units, so consecutive units
   // mostly share a request and its record is fetched once
+  const int W = gridDim.x * kWavesPerBlock;
   const long long n_units = (long long)a.ws.hdr->n_resid * a.nrseg;
   const int u_begin = (int)(n_units * gw / W);
   const int u_end = (int)(n_units * (gw + 1) / W);
@@ -720,42 +761,50 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
 // The draw above evaluates the weights in fp32 (exp2 with the fp32 scale c, so
 // at the temperature log2(e)/c; reciprocals of the row sums rounded to fp32;
 // lane sums of a few dozen fp32 terms) and locates the crossing of w * Z in
-// fp64 over them.  Its cumulative masses then differ from the exact ones at
-// temperature T by less than about 1.1e-5 of probability mass in the worst
-// case (temperature 2^-24 relative, <= 2 ln(V) * 2^-24 per row; rounding and
-// exp2 <= 2^-20; row sums <= 40 * 2^-24 relative per row).  A draw whose
-// crossing lies farther than kCertMargin from both edges of the chosen id's
-// interval is therefore the exact draw.  Otherwise (a crossing closer than
-// that, no crossing found, or a residual total that rounded to 0) the whole
-// workgroup redoes the draw from the logits in fp64: p_v = exp((z_v - M)/T)/S
-// with S summed in fp64, the residual [p_v - q_v]_+ formed from those fp64
-// values (no cancellation to speak of at any residual total), its total, and
-// the first id whose running sum exceeds w times that total.  Such draws are
-// rare (a margin below 2^-15 of a residual total Z happens with probability
-// about 2^-14 / Z) and take several fp64 passes over the row pair on one CU.
+// fp64 over them.  Its cumulative masses differ from the exact ones at
+// temperature T by about 1e-8 of the probability mass on typical rows; the
+// errors of single exp2 evaluations, of the row sums and the 2^-24 relative
+// temperature of the fp32 scale keep it below 1e-7 unless a row has extreme
+// spread, and below about 1.1e-5 for any row (temperature <= 2 ln(V) 2^-24
+// per row, rounding and exp2 <= 2^-20, row sums <= 40 2^-24 relative).
+// Contract: the draw equals the exact draw unless the exact crossing lies
+// within 1e-6 of the total of the weights from an edge of the chosen id's
+// interval (then either neighbour may come back).
+//  - a draw from p (bonus) or from a residual whose fp32 total is at least
+//    kSmallResidual: an error of 1e-7 of the mass is below 1e-6 of the total,
+//    so the fp32 draw keeps the contract;
+//  - a residual total below that: the fp32 draw is kept when its crossing
+//    lies farther than kCertMargin (above the any-row bound) from both edges;
+//  - otherwise, and whenever no id crossed w * Z or the fp32 residual total
+//    was 0, the whole workgroup redoes the draw from the logits in fp64:
+//    p_v = exp((z_v - M)/T)/S with S summed in fp64, the residual
+//    [p_v - q_v]_+ formed from those fp64 values (no cancellation to speak of
+//    at any total), its total, and the first id whose running sum exceeds
+//    w times that total.  That takes several fp64 passes over the row pair on
+//    one CU; it happens only for rows where p and q nearly agree.
+constexpr double kSmallResidual = 0.125;
 constexpr double kCertMargin = 0x1p-15;
-constexpr int kFusedWavesMax = 16;      // largest workgroup that runs a draw: 1024 threads
-
 struct FinalizeShared {
   double wave[kWavesPerBlock];
   double before, thr, Z;
   int unit, mode, fallback, owner;
   int tok, cert;                  // the fp32 draw and whether its margin certifies it
-  double red[kFusedWavesMax];     // fp64 draw: wave totals of a block scan or sum
+  double red[kWavesPerBlock];     // fp64 draw: wave totals of a block scan or sum
   int ptok, found, plast;
 };
 
-// Sum of x over the workgroup, in the same order in every thread.
+// Sum of x over the first kBlock threads of the workgroup, in the same order
+// in every thread and for any workgroup size (threads past kBlock take part
+// in the barriers only).
 __device__ double block_sum(double x, double* red) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
   x = wave_sum(x);
   __syncthreads();                      // red may still be read by an earlier call
-  if (lane == 0) red[wv] = x;
+  if (lane == 0 && wv < kWavesPerBlock) red[wv] = x;
   __syncthreads();
   double t = 0.0;
-  for (int q = 0; q < nw; ++q) t += red[q];
+  for (int q = 0; q < kWavesPerBlock; ++q) t += red[q];
   return t;
 }
 
@@ -789,10 +838,12 @@ __device__ __forceinline__ void visit_ids(const typename L::Elem* tp, const type
   for (; v < v0 + n; ++v) f(v, L::one(tp + v), dp ? L::one(dp + v) : 0.f);
 }
 
-// The draw in fp64 by the whole workgroup (every thread calls it; the result
-// is valid in every thread).  resid: weights [p - q]_+ (falling back to p if
-// their total is 0), else p.  Returns the token; *Z = total of the residual
-// weights (0 after the fallback) or of p.
+// The draw in fp64 by the workgroup (every thread calls it; the result is
+// valid in every thread).  The ids are split over the first kBlock threads
+// whatever the workgroup size, so every launch plan sums in the same order.
+// resid: weights [p - q]_+ (falling back to p if their total is 0), else p.
+// Returns the token; *Z = total of the residual weights (0 after the
+// fallback) or of p.
 template <class L>
 __device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* dp, int V,
                             double Mp, double Mq, double T, double w, bool resid, double* Z,
@@ -800,7 +851,8 @@ __device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* 
   constexpr int E = L::E;
   constexpr int SLOT = E * 4;           // consecutive ids per thread and tile
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
+  const int nthr = kBlock;              // threads with work; the others idle
+  const bool active = tid < nthr;
   const int lane = tid & (kWave - 1);
   const int wv = tid >> 6;
   const int nslot = (V + SLOT - 1) / SLOT;
@@ -814,7 +866,7 @@ __device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* 
     sp += exp(((double)z - Mp) / T);
     if (resid) sq += exp(((double)d - Mq) / T);
   };
-  for (int sl = tid; sl < nslot; sl += nthr)
+  for (int sl = tid; active && sl < nslot; sl += nthr)
     visit_ids<L>(tp, resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), sums);
   pw.Sp = block_sum(sp, sh.red);
   pw.Sq = resid ? block_sum(sq, sh.red) : 1.0;
@@ -827,7 +879,7 @@ __device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* 
     tq += pp(z, d);
     if (resid) tr += pw(z, d);
   };
-  for (int sl = tid; sl < nslot; sl += nthr)
+  for (int sl = tid; active && sl < nslot; sl += nthr)
     visit_ids<L>(tp, resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), totals);
   const double Ptot = block_sum(tq, sh.red);
   double total = Ptot;
@@ -856,22 +908,23 @@ __device__ int precise_draw(const typename L::Elem* tp, const typename L::Elem* 
       ts += x;
       if (x > 0.0) tl = v;
     };
-    if (sl < nslot) visit_ids<L>(tp, pw.resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), acc);
+    if (active && sl < nslot)
+      visit_ids<L>(tp, pw.resid ? dp : nullptr, sl * SLOT, min(SLOT, V - sl * SLOT), acc);
     if (tl >= 0) mylast = tl;
     const double iw = wave_incl_scan(ts, lane);
     __syncthreads();
-    if (lane == kWave - 1) sh.red[wv] = iw;
+    if (lane == kWave - 1 && wv < kWavesPerBlock) sh.red[wv] = iw;
     if (tid == 0) sh.owner = INT_MAX;
     __syncthreads();
     double pre = 0.0, tile = 0.0;
-    for (int q = 0; q < (nthr >> 6); ++q) {
+    for (int q = 0; q < kWavesPerBlock; ++q) {
       if (q < wv) pre += sh.red[q];
       tile += sh.red[q];
     }
     const double prev = __shfl_up(iw, 1);
     const double excl = carry + pre + (lane == 0 ? 0.0 : prev);
     const double incl = carry + pre + iw;
-    if (sl < nslot && incl > thr && ts > 0.0) atomicMin(&sh.owner, tid);
+    if (active && sl < nslot && incl > thr && ts > 0.0) atomicMin(&sh.owner, tid);
     __syncthreads();
     if (tid == sh.owner) {
       double cum = excl;
@@ -963,9 +1016,12 @@ __device__ __forceinline__ void finalize_request(const Args& a, int b, const Req
   }
   if (tok != -2) {
     sh.tok = tok;
-    // a residual draw that fell back to p because its fp32 total was 0 is
-    // never certified: the exact total may be positive
-    sh.cert = (fm > kCertMargin && (R.kind != KIND_RESID || mode == DRAW_RESID)) ? 1 : 0;
+    // (a residual draw that fell back to p because its fp32 total was 0 is
+    // never kept: the exact total may be positive)
+    const bool crossed = fm >= 0.0;
+    const bool resid = R.kind == KIND_RESID;
+    sh.cert = (crossed && !(resid && mode != DRAW_RESID) &&
+               (!resid || sh.Z >= kSmallResidual || fm > kCertMargin)) ? 1 : 0;
   }
   __syncthreads();
   if (sh.cert) {
@@ -1491,8 +1547,8 @@ __global__ __launch_bounds__(kBlock) void k_decide_round(Args a) {
 // ------------------------------------------------------------------ host side
 
 struct Sizes {
-  size_t off_hdr, off_req, off_rowdesc, off_resid, off_pt, off_pd, off_rp, off_rows_r, off_res_r,
-      off_alive, total;
+  size_t off_hdr, off_req, off_rowdesc, off_rowdesc_b, off_resid, off_pt, off_pd, off_rp,
+      off_rows_r, off_res_r, off_alive, total;
 };
 
 bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
@@ -1507,6 +1563,7 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
   z->off_hdr = o; o = align_up(o + sizeof(Header), 256);
   z->off_req = o; o = align_up(o + sizeof(ReqInfo) * (size_t)B, 256);
   z->off_rowdesc = o; o = align_up(o + 4 * (size_t)(2 * K + B), 256);
+  z->off_rowdesc_b = o; o = align_up(o + 4 * (size_t)(2 * B), 256);
   z->off_resid = o; o = align_up(o + 4 * (size_t)B, 256);
   z->off_pt = o; o = align_up(o + sizeof(Partial) * (size_t)((K + B) * nseg), 256);
   z->off_pd = o; o = align_up(o + sizeof(Partial) * (size_t)(K * nseg), 256);
@@ -1661,6 +1718,7 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.ws.hdr = reinterpret_cast<Header*>(wb + z.off_hdr);
   a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);
   a.ws.rowdesc = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc);
+  a.ws.rowdesc_b = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc_b);
   a.ws.resid_list = reinterpret_cast<int*>(wb + z.off_resid);
   a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
   a.ws.pd = reinterpret_cast<Partial*>(wb + z.off_pd);
@@ -1671,6 +1729,8 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.ws.alive_e = reinterpret_cast<AliveEntry*>(wb + z.off_alive);
   a.rowlist = a.ws.rowdesc;
   a.rowcount = &a.ws.hdr->n_rows;
+  a.rowlist_b = a.ws.rowdesc_b;
+  a.rowcount_b = &a.ws.hdr->n_rows_b;
   a.ee_round = -1;
   a.ee_lo = a.ee_hi = a.ee_nhi = 0;
   a.max_k = max_k;

@@ -115,13 +115,19 @@ def inverse_cdf(weights: np.ndarray, w: float):
 
 def verify_request(target_rows: np.ndarray, draft_rows: Optional[np.ndarray],
                    tokens: np.ndarray, greedy: bool, T: Optional[float],
-                   u_accept: np.ndarray, w: float) -> dict:
+                   u_accept: np.ndarray, w: float, early_exit: bool = False) -> dict:
     """One request: k drafts, k+1 target rows, left-to-right verification.
 
     Returns accepted length a (excludes the final token), the committed tokens
     (a drafts + the correction or bonus), p(y_i) / q(y_i) for every draft row
     (stochastic requests; -1 for greedy ones), the residual mass Z (-1 when the
-    bonus was drawn or the request is greedy) and the smallest decision margin.
+    bonus was drawn or the request is greedy) and the smallest decision margin
+    (over the ratio tests up to the cut and the final draw).
+
+    early_exit: compute the distributions of a position only when its test is
+    reached (drafts after the first rejection are discarded unread, [VLLM]
+    "Core idea of speculative decoding"); p(y_i), q(y_i) are then -1 after
+    the cut, everything else is the same.
     """
     k = int(len(tokens))
     assert target_rows.shape[0] == k + 1
@@ -142,20 +148,30 @@ def verify_request(target_rows: np.ndarray, draft_rows: Optional[np.ndarray],
     for y in tokens:
         if not (0 <= int(y) < V):
             raise ValueError(f"draft token {int(y)} outside [0, {V})")
-    ps = [tempered_softmax(target_rows[i], T) for i in range(k)]
-    qs = [tempered_softmax(draft_rows[i], T) for i in range(k)]
-    for i in range(k):
-        p_y[i] = ps[i][int(tokens[i])]
-        q_y[i] = qs[i][int(tokens[i])]
+    ps, qs = {}, {}
+
+    def dists(i):
+        """p_i, q_i of position i (computed once), with p(y_i), q(y_i)."""
+        if i not in ps:
+            ps[i] = tempered_softmax(target_rows[i], T)
+            qs[i] = tempered_softmax(draft_rows[i], T)
+            p_y[i] = ps[i][int(tokens[i])]
+            q_y[i] = qs[i][int(tokens[i])]
+        return ps[i], qs[i]
+
+    if not early_exit:
+        for i in range(k):
+            dists(i)
     margin = math.inf
     for i in range(k):
+        p_i, q_i = dists(i)
         margin = min(margin, accept_margin(u_accept[i], p_y[i], q_y[i]))
         if not keeps_draft(u_accept[i], p_y[i], q_y[i]):
-            r = positive_residual(ps[i], qs[i])
+            r = positive_residual(p_i, q_i)
             if float(np.cumsum(r)[-1]) > 0.0:
                 t, Z, m = inverse_cdf(r, w)
             else:                                   # reading R6
-                t, _, m = inverse_cdf(ps[i], w)
+                t, _, m = inverse_cdf(p_i, w)
                 Z = 0.0
             return dict(a=i, committed=[int(x) for x in tokens[:i]] + [t],
                         p_y=p_y, q_y=q_y, resid_mass=Z, margin=min(margin, m))
@@ -166,7 +182,7 @@ def verify_request(target_rows: np.ndarray, draft_rows: Optional[np.ndarray],
 
 
 def verify_batch(target, draft, tokens, num_draft, greedy, temperature,
-                 u_accept, u_final) -> dict:
+                 u_accept, u_final, early_exit: bool = False) -> dict:
     """A packed batch (layout of the C ABI) -> per-request results.
 
     target: [K+B, V], row of (b, i) = off[b] + b + i;  draft: [K, V] or None,
@@ -192,7 +208,7 @@ def verify_batch(target, draft, tokens, num_draft, greedy, temperature,
             np.asarray(target[t0:t0 + k + 1]),
             None if greedy[b] else np.asarray(draft[d0:d0 + k]),
             np.asarray(tokens[d0:d0 + k]), bool(greedy[b]), temperature,
-            np.asarray(u_accept[d0:d0 + k]), float(u_final[b]))
+            np.asarray(u_accept[d0:d0 + k]), float(u_final[b]), early_exit)
         acc[b] = res["a"]
         out[t0:t0 + len(res["committed"])] = res["committed"]
         p_y[d0:d0 + k] = res["p_y"]

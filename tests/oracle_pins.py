@@ -367,9 +367,43 @@ def pin_decision_margins(vm):
     assert math.isinf(_run(vm, tgt, None, [3, 0], True, None, [0, 0], 0.5)["margin"])
 
 
+def pin_early_exit_form(vm, n_batches: int = 6, seed: int = 31):
+    """The left-to-right form that computes a position's distributions only
+    when its test is reached gives the same decisions, tokens, residual masses
+    and margins as the form that computes every row, and p(y), q(y) at the
+    tested positions (-1 after the cut)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(n_batches):
+        B, V = 12, int(rng.integers(2, 60))
+        ks = rng.integers(0, 6, size=B)
+        K = int(ks.sum())
+        off = np.concatenate([[0], np.cumsum(ks)])
+        tgt = rng.normal(0, 2.0, size=(K + B, V))
+        dr = np.zeros((K, V))
+        for b in range(B):
+            for i in range(int(ks[b])):      # draft row (b, i) = target row (b, i) + noise
+                dr[off[b] + i] = tgt[off[b] + b + i] + rng.normal(0, 0.7, size=V)
+        toks = rng.integers(0, V, size=K)
+        greedy = rng.random(B) < 0.3
+        u, wf = rng.random(K), rng.random(B)
+        full = vm.verify_batch(tgt, dr, toks, ks, greedy, 0.9, u, wf)
+        ee = vm.verify_batch(tgt, dr, toks, ks, greedy, 0.9, u, wf, early_exit=True)
+        for key in ("accepted_len", "out_tokens", "resid_mass", "margin"):
+            assert np.array_equal(full[key], ee[key]), key
+        for b in range(B):
+            if greedy[b]:
+                continue
+            n = min(int(full["accepted_len"][b]) + 1, int(ks[b]))
+            s0 = slice(int(off[b]), int(off[b]) + n)
+            s1 = slice(int(off[b]) + n, int(off[b + 1]))
+            for key in ("p_draft", "q_draft"):
+                assert np.array_equal(ee[key][s0], full[key][s0])
+                assert np.all(ee[key][s1] == -1.0) and np.all(full[key][s1] >= 0.0)
+
+
 ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ties,
             pin_exact_distribution_quadrature, pin_special_cases, pin_greedy_invariants,
-            pin_packed_batch, pin_decision_margins]
+            pin_packed_batch, pin_decision_margins, pin_early_exit_form]
 
 
 # ---------------------------------------------------------------- acceptance statistics

@@ -13,9 +13,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.mark.timeout(600)
 def test_default_bench_line():
-    print("[bench] python bench.py --steps 5 --warmup 2 --cpu-seconds 1", flush=True)
+    print("[bench] python bench.py --steps 5 --warmup 2", flush=True)
     r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "5",
-                        "--warmup", "2", "--cpu-seconds", "1"],
+                        "--warmup", "2"],
                        capture_output=True, text=True, timeout=540, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
     line = json.loads(r.stdout.strip().splitlines()[-1])
@@ -31,3 +31,11 @@ def test_default_bench_line():
     assert 0 < rf["achieved"] < rf["peak"] and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     cb = line["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    assert cb["variants"] and all(v["value"] > 0 for v in cb["variants"].values())
+    par = line["parity"]
+    assert par["requests"] == 512 and par["mismatches"] == 0, par
+    cf = line["configs"]
+    assert len(cf) == 5 and "ragged_mixed_v262144" in cf
+    for name, c in cf.items():
+        assert c["step_us"] > 0 and c["positions_per_s"] >= 0, name
+        assert c["parity"]["mismatches"] == 0, (name, c["parity"])

@@ -117,9 +117,9 @@ def test_moderate_residual_totals():
 
 def test_draws_near_an_interval_edge():
     """Uniforms placed within 1e-9 .. 1e-5 of a cumulative edge of the bonus
-    distribution (k = 0): the fp32 margin is below the certification bound, so
-    these draws run in fp64 and must still match the oracle (margins above
-    1e-6 relative) or be near-ties (below)."""
+    distribution (k = 0): the fp32 draw is kept for draws from p, so this
+    checks its accuracy where it matters most: every draw whose exact margin
+    is 1e-6 of the total or more must match the oracle."""
     import scipy.special
     rng = np.random.default_rng(21)
     V, B = 4099, 24

@@ -45,6 +45,10 @@ def test_decision_margins():
     pins.pin_decision_margins(vm)
 
 
+def test_early_exit_form():
+    pins.pin_early_exit_form(vm)
+
+
 def test_packed_ragged_batch():
     pins.pin_packed_batch(vm)
 
