@@ -31,7 +31,11 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
             "spec_verify_set_profile_events", "spec_verify_tree_workspace_bytes",
             "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit",
             "spec_verify_adaptive_length", "spec_verify_gather_rows",
-            "spec_verify_set_launch_plan")
+            "spec_verify_set_launch_plan", "spec_verify_sample_noalloc")
+
+# SPEC_VERIFY_NOALLOC_MAX_BYTES of the C header: the largest workspace that
+# spec_verify_sample_noalloc serves from its static device array.
+NOALLOC_MAX_BYTES = 32 << 20
 
 
 class SvBatch(ctypes.Structure):
@@ -81,6 +85,9 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_sample_early_exit.argtypes = [ctypes.POINTER(SvBatch), i32, ctypes.c_float,
                                                   vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_sample_early_exit.restype = i32
+    lib.spec_verify_sample_noalloc.argtypes = [ctypes.POINTER(SvBatch), ctypes.c_float, vp, vp, vp,
+                                               vp, vp, vp, vp, vp, vp]
+    lib.spec_verify_sample_noalloc.restype = i32
     lib.spec_verify_accept_stats.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.spec_verify_accept_stats.restype = i32
     lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32]
@@ -247,6 +254,30 @@ def spec_verify_sample(target: torch.Tensor, draft: Optional[torch.Tensor],
         st = lib().spec_verify_sample(ctypes.byref(bt), *rest)
     else:
         st = lib().spec_verify_sample_early_exit(ctypes.byref(bt), int(max_k), *rest)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,
+                q_draft=q_draft, resid_mass=resid_mass)
+
+
+def spec_verify_sample_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor],
+                               draft_tokens: torch.Tensor, num_draft: torch.Tensor,
+                               temperature: float, u_accept: torch.Tensor, u_final: torch.Tensor,
+                               *, greedy_mask=None, accepted_len=None, out_tokens=None,
+                               p_draft=None, q_draft=None, resid_mass=None, stream=None):
+    """spec_verify_sample with the library's static device workspace (the C
+    call allocates nothing; pass preallocated outputs to allocate nothing at
+    all).  Returns the same dict of device tensors."""
+    bt = make_batch_struct(target, draft, draft_tokens, num_draft)
+    dev = target.device
+    if accepted_len is None:
+        accepted_len = torch.empty(bt.B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty(bt.K + bt.B, dtype=torch.int32, device=dev)
+    st = lib().spec_verify_sample_noalloc(
+        ctypes.byref(bt), ctypes.c_float(temperature), _ptr(greedy_mask), _ptr(u_accept),
+        _ptr(u_final), _ptr(accepted_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+        _ptr(resid_mass), _stream_handle(stream))
     if st != SV_OK:
         raise SpecVerifyError(st)
     return dict(accepted_len=accepted_len, out_tokens=out_tokens, p_draft=p_draft,

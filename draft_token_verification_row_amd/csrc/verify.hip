@@ -44,6 +44,8 @@
 // (lexicographic max of (value, -id)).
 #include "sv_common.hpp"
 
+#include <mutex>
+
 namespace {
 
 // ------------------------------------------------------------------ k_plan
@@ -1773,6 +1775,54 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
 
 
 }  // namespace
+
+// ------------------------------------------------------------------ no-allocation entry point
+// Workspace of spec_verify_sample_noalloc: one array of SPEC_VERIFY_NOALLOC_MAX_BYTES
+// on every device the library runs on, held until the process ends.  In host
+// code `scratch` only stands for the symbol; its device address on the current
+// device comes from hipGetSymbolAddress, taken once per device and kept in
+// g_scratch_addr, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SPEC_VERIFY_NOALLOC_MAX_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device dev (the current device).
+int32_t scratch_address(int dev, void** addr) {
+  if (dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return SV_OK;
+}
+}  // namespace
+
+extern "C" int32_t spec_verify_sample_noalloc(const sv_batch_t* batch, float temperature,
+                                              const uint8_t* greedy_mask, const float* u_accept,
+                                              const float* u_final, int32_t* accepted_len,
+                                              int32_t* out_tokens, float* p_draft, float* q_draft,
+                                              float* resid_mass, void* stream) {
+  if (!batch) return SV_ERR_INVALID_ARG;
+  Sizes z;
+  if (!compute_sizes(batch->B, batch->K, batch->V, &z)) return SV_ERR_INVALID_ARG;
+  if (z.total > (size_t)SPEC_VERIFY_NOALLOC_MAX_BYTES) return SV_ERR_WORKSPACE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+  void* ws = nullptr;
+  const int32_t st = scratch_address(dev, &ws);
+  if (st != SV_OK) return st;
+  return run(batch, true, temperature, greedy_mask, u_accept, u_final, accepted_len, out_tokens,
+             p_draft, q_draft, resid_mass, ws, (size_t)SPEC_VERIFY_NOALLOC_MAX_BYTES, stream, false, 0);
+}
 
 
 extern "C" size_t spec_verify_workspace_bytes(int32_t B, int32_t K, int32_t V) {

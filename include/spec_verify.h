@@ -33,8 +33,10 @@
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers on the current HIP device, owned
  *     by the caller.  The library allocates nothing and keeps no state between
- *     calls; calls are asynchronous on `stream` (a hipStream_t, NULL = the
- *     default stream) and results are valid once the stream reaches the call.
+ *     calls (apart from the static device array that spec_verify_sample_noalloc
+ *     uses in place of a workspace); calls are asynchronous on `stream` (a
+ *     hipStream_t, NULL = the default stream) and results are valid once the
+ *     stream reaches the call.
  *     Outputs must not overlap the inputs, each other or the workspace; two
  *     calls in flight at once need two workspaces.
  *   - Host-side argument checks run before any HIP call.  A failed check
@@ -50,9 +52,16 @@
  *     (target or draft) whose logits are all -inf is reported like one with
  *     an invalid token; rows after its cut are not looked at.  NaN / +inf
  *     give unspecified (but in-range or -1) results.
- *   - Temperature: every kernel uses the one fp32 scale c = fl(log2(e)/T), so
- *     the distributions are softmax(z / T') with T' = log2(e)/c, within a
- *     relative 2^-24 of T.
+ *   - Temperature: the fp32 arithmetic uses the one scale c = fl(log2(e)/T),
+ *     i.e. softmax(z / T') with T' = log2(e)/c within a relative 2^-24 of T;
+ *     p(y), q(y) and the ratio tests are evaluated in fp64 from fp32 row sums.
+ *   - The final draw equals the exact draw (at temperature T) unless the
+ *     exact crossing of w_b * total lies within 1e-6 of the total from an edge
+ *     of the chosen id's cumulative interval: draws from p and from residuals
+ *     whose total is at least 1/8 are made with fp32 weights (cumulative
+ *     error about 1e-8, below 1e-7 of the mass), smaller residuals are redone
+ *     in fp64 from the logits unless the fp32 crossing lies clear of both
+ *     edges.
  *   - Unused out_tokens slots (after the committed a_b + 1 tokens) are -1.
  *   - No C++ exception crosses this interface.
  */
@@ -284,6 +293,26 @@ int32_t spec_verify_adaptive_length(int32_t B, int32_t N, const float* conf,
 int32_t spec_verify_gather_rows(int32_t dtype, int32_t V, const void* src, int64_t src_ld,
                                 int32_t src_rows, const int32_t* index, const int32_t* count,
                                 int32_t max_rows, void* dst, int64_t dst_ld, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * spec_verify_sample with the same arguments and results, minus the workspace,
+ * which is a static device array of SPEC_VERIFY_NOALLOC_MAX_BYTES that the
+ * library holds on every device it runs on until the process ends.  The call
+ * allocates nothing and returns SV_ERR_WORKSPACE (launching and writing
+ * nothing) when spec_verify_workspace_bytes(B, K, V) exceeds that size (for
+ * example B = 2048 requests with 8 drafts each at V = 262144 fit).  Every call
+ * on one device uses the same array, which keeps the last call's contents:
+ * calls that overlap on one device (two streams, two host threads) race and
+ * must be serialised by the caller.  Launch plan and results as for
+ * spec_verify_sample. */
+#define SPEC_VERIFY_NOALLOC_MAX_BYTES (32u << 20)
+int32_t spec_verify_sample_noalloc(const sv_batch_t* batch, float temperature,
+                                   const uint8_t* greedy_mask,
+                                   const float* u_accept, const float* u_final,
+                                   int32_t* accepted_len, int32_t* out_tokens,
+                                   float* p_draft, float* q_draft, float* resid_mass,
+                                   void* stream);
 
 /* Launch plan of spec_verify_greedy / spec_verify_sample for calls made from
  * the calling thread: 0 = automatic (default: one launch, one workgroup per
