@@ -2,21 +2,23 @@
 blog post "speculative-decoding-amd-gpus", Appendix (per target model, drafting
 method and dataset: one table row per proposal length N with the speed-up, the
 throughput, MAL, AR and the per-position acceptance p1..pN in percent, as
-printed).  Run once by hand where the page text is available:
+printed).  Run once by hand where a text copy of the page is available:
 
-    python tests/golden/extract_appendix.py /root/reference/PAPER.md
+    python tests/golden/extract_appendix.py PAGE_TEXT [--exclude-model NAME ...]
 
-The committed JSON is what the tests read; nothing reads the page at test time.
+--exclude-model leaves out every table whose target model is NAME (the part
+of the table title before the first " / ").  The committed JSON is what the
+tests read; nothing reads the page at test time.
 """
+import argparse
 import json
 import os
 import re
-import sys
 
 ROW = re.compile(r"^N=(\d+)\s+([0-9.]+)x\s*\|\s*([0-9,]+)\s*tok/sMAL\s+([0-9.]+)\s*\|\s*AR\s+([0-9.]+)%\s*(.*)$")
 
 
-def main(path):
+def main(path, exclude=()):
     lines = open(path, encoding="utf-8").read().splitlines()
     start = next(i for i, l in enumerate(lines) if l.strip() == "Appendix")
     rows, table = [], None
@@ -26,7 +28,7 @@ def main(path):
             table = s
             continue
         m = ROW.match(s)
-        if m and table:
+        if m and table and table.split(" / ")[0] not in exclude:
             N = int(m.group(1))
             p = [int(x) for x in re.findall(r"(\d+)%", m.group(6))]
             if len(p) != N:
@@ -43,4 +45,8 @@ def main(path):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1])
+    ap = argparse.ArgumentParser()
+    ap.add_argument("page_text")
+    ap.add_argument("--exclude-model", action="append", default=[])
+    args = ap.parse_args()
+    main(args.page_text, tuple(args.exclude_model))

@@ -408,13 +408,13 @@ ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ti
 
 # ---------------------------------------------------------------- acceptance statistics
 def pin_acceptance_appendix(am, B: int = 20000):
-    """All 400 rows of the [VLLM] Appendix tables: rounds built so that
+    """All 356 rows of the [VLLM] Appendix tables in the fixture: rounds built so that
     #{A >= j} / B equals each printed p_j reproduce the printed MAL and AR
     (MAL counts the final token, AR = (MAL - 1) / N), within the rounding of
     the printing: p_j whole percent (so MAL within N * 0.005 + 0.005) and AR
     one decimal percent (within 0.5 + 0.05 points)."""
     g = load_golden("appendix_acceptance_all.json")
-    assert len(g["rows"]) == 400
+    assert len(g["rows"]) == 356
     for r in g["rows"]:
         N = r["N"]
         c = [int(round(p / 100.0 * B)) for p in r["p"]] + [0]
