@@ -101,7 +101,7 @@ struct Header {
   int error;
   int n_rows;
   int n_units;
-  int n_resid;
+  int n_stoch;        // stochastic requests (listed in Workspace::stoch_list)
   int n_rows3[3];     // early-exit rounds: rows listed for a round (three lists in rotation)
   int n_res3[3];      // early-exit rounds: residual sweeps listed for a round
   int n_alive3[3];    // early-exit rounds: requests deciding a position in the round
@@ -114,7 +114,7 @@ struct Workspace {
   ReqInfo* req;
   uint32_t* rowdesc;   // [2K + B]
   uint32_t* rowdesc_b; // [2B]  rows streamed last (position-0 pairs of stochastic requests)
-  int* resid_list;     // [B]
+  int* stoch_list;     // [B]   the stochastic requests, in request order
   Partial* pt;         // [(K + B) * nseg]
   Partial* pd;         // [K * nseg]
   double* rp;          // [B * nrseg]
@@ -147,6 +147,7 @@ struct Args {
   const int* rowcount;       // number of rows in rowlist
   const uint32_t* rowlist_b = nullptr;   // rows k_stats reads after those, or NULL
   const int* rowcount_b = nullptr;       // number of rows in rowlist_b (when not NULL)
+  int plan_in_kernel = 0;    // k_stats plans the call itself (no rowlist; see plan_block)
   int ee_round;              // early-exit round, -1 on the all-rows path
   int ee_lo, ee_hi, ee_nhi;  // early exit: positions [lo, hi) decided in this round, [hi, nhi) in the next
   int max_k;                 // early-exit: bound on every num_draft[b] (trees: on every depth)
@@ -439,21 +440,206 @@ __device__ __forceinline__ Scan2 block_scan2(long long v0, long long v1, long lo
   return r;
 }
 
+// ------------------------------------------------------------------ row lists
+// The rows an all-rows call streams, in two lists that k_stats reads in
+// order.  The second list holds the position-0 (target, draft) pair of every
+// stochastic request with k_b >= 1: about half of all cuts fall at position 0
+// and the residual sweep re-reads exactly the rejected pair, so those pairs
+// are read last.  The first list holds every other row, request after
+// request: all target rows of a greedy request; target rows 1..k_b then draft
+// rows 1..k_b-1 of a stochastic request (its target row 0 when k_b = 0).
+__device__ __forceinline__ void row_counts(int k, bool g, int& cA, int& cB) {
+  const bool pair0 = SV_MALL_ORDER && !g && k >= 1;
+  cA = g ? k + 1 : (pair0 ? 2 * k - 1 : 2 * k + 1);
+  cB = pair0 ? 2 : 0;
+}
+
+// Descriptor of entry j of request b in the first list (off = its offset).
+__device__ __forceinline__ uint32_t row_in_first(int b, int j, int off, int k, bool g) {
+  if (g) return (uint32_t)(off + b + j) | kGreedyBit;
+  const int first = (SV_MALL_ORDER && k >= 1) ? 1 : 0;   // position 0 in the second list
+  const int nt = k + 1 - first;                            // target rows of the first list
+  return j < nt ? (uint32_t)(off + b + first + j)
+                : ((uint32_t)(off + first + (j - nt)) | kDraftBit);
+}
+
+// Descriptor of entry j (0: target, 1: draft) of request b in the second list.
+__device__ __forceinline__ uint32_t row_in_second(int b, int j, int off) {
+  return j == 0 ? (uint32_t)(off + b) : ((uint32_t)off | kDraftBit);
+}
+
+// Plan of one call made by every k_stats workgroup when it fits in LDS
+// (plan_fits_lds): the exclusive prefix sums over the requests of k_b, of
+// their first-list rows and of their second-list rows, and from them the
+// table of every row descriptor to stream (first list, then second list), so
+// that finding a unit's row is one LDS read.
+constexpr int kPlanInKernelMaxB = 2048;     // requests (8 per thread of a workgroup)
+constexpr int kPlanInKernelMaxRows = 6144;  // row descriptors (24 KiB of LDS)
+
+__host__ __device__ constexpr bool plan_fits_lds(long long B, long long K) {
+  return B <= kPlanInKernelMaxB && 2 * K + B <= kPlanInKernelMaxRows;
+}
+
+__host__ __device__ constexpr size_t plan_lds_bytes(long long B, long long K) {
+  return (size_t)(2 * K + B) * sizeof(uint32_t);
+}
+
+struct Sums4 {
+  int k, a, b, s;
+};
+
+__device__ __forceinline__ Sums4 wave_incl_scan4(Sums4 x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int k = __shfl_up(x.k, o), a = __shfl_up(x.a, o);
+    const int b = __shfl_up(x.b, o), s = __shfl_up(x.s, o);
+    if (lane >= o) {
+      x.k += k;
+      x.a += a;
+      x.b += b;
+      x.s += s;
+    }
+  }
+  return x;
+}
+
+// Every thread of the k_stats workgroup (kBlock threads) takes part: thread t
+// plans the requests [t * per, (t + 1) * per), per = ceil(B / kBlock) <= 8,
+// and writes their rows to table (first list at [0, nA), second list at
+// [nA, nA + nB)).  Returns false when num_draft is inconsistent (a k_b < 0 or
+// > K, or a total other than K); nA, nB are then 0.  records: also write the
+// request records, the list of stochastic requests and the header (one
+// workgroup does).
+__device__ bool plan_block(const Args& a, uint32_t* table, bool records, int& nA, int& nB) {
+  __shared__ Sums4 s_w[kWavesPerBlock];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid >> 6;
+  const int B = a.B;
+  const int per = (B + kBlock - 1) / kBlock;
+  const int b0 = tid * per;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  constexpr int kPer = kPlanInKernelMaxB / kBlock;
+  int kk[kPer];
+  bool gg[kPer];
+  Sums4 mine = {0, 0, 0, 0};
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    kk[q] = 0;
+    gg[q] = true;
+    const int b = b0 + q;
+    if (q < per && b < B) {
+      int k = a.num_draft[b];
+      if (k < 0 || k > a.K) {
+        bad = true;
+        k = 0;
+      }
+      const bool g = a.force_greedy ? true : (a.gmask ? (a.gmask[b] != 0) : false);
+      int cA, cB;
+      row_counts(k, g, cA, cB);
+      kk[q] = k;
+      gg[q] = g;
+      mine.k += k;
+      mine.a += cA;
+      mine.b += cB;
+      mine.s += g ? 0 : 1;
+    }
+  }
+  if (bad) s_bad = 1;
+  const Sums4 inc = wave_incl_scan4(mine, lane);
+  if (lane == kWave - 1) s_w[wv] = inc;
+  __syncthreads();
+  Sums4 ex = {inc.k - mine.k, inc.a - mine.a, inc.b - mine.b, inc.s - mine.s};
+  Sums4 tot = {0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < kWavesPerBlock; ++q) {
+    const Sums4 w = s_w[q];
+    if (q < wv) {
+      ex.k += w.k;
+      ex.a += w.a;
+      ex.b += w.b;
+      ex.s += w.s;
+    }
+    tot.k += w.k;
+    tot.a += w.a;
+    tot.b += w.b;
+    tot.s += w.s;
+  }
+  const bool ok = !s_bad && tot.k == a.K;   // then every table index stays below 2K + B
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int b = b0 + q;
+    if (q < per && b < B) {
+      int cA, cB;
+      row_counts(kk[q], gg[q], cA, cB);
+      if (ok) {
+        for (int j = 0; j < cA; ++j) table[ex.a + j] = row_in_first(b, j, ex.k, kk[q], gg[q]);
+        for (int j = 0; j < cB; ++j) table[tot.a + ex.b + j] = row_in_second(b, j, ex.k);
+      }
+      if (records) {
+        ReqInfo r;
+        r.off = ex.k;
+        r.k = kk[q];
+        r.greedy = gg[q] ? 1 : 0;
+        r.a = 0;
+        r.kind = KIND_NONE;
+        r.y = -1;
+        r.trow = -1;
+        r.drow = -1;
+        r.Mp = r.Mq = 0.f;
+        r.pad0 = r.pad1 = 0;
+        r.Sp = r.Sq = 0.0;
+        a.ws.req[b] = r;
+        if (!gg[q]) a.ws.stoch_list[ex.s] = b;
+      }
+      ex.k += kk[q];
+      ex.a += cA;
+      ex.b += cB;
+      ex.s += gg[q] ? 0 : 1;
+    }
+  }
+  if (records && tid == 0) {
+    Header* h = a.ws.hdr;
+    h->error = ok ? 0 : 1;
+    h->n_rows = ok ? tot.a : 0;
+    h->n_rows_b = ok ? tot.b : 0;
+    h->n_stoch = ok ? tot.s : 0;
+    h->n_units = 0;
+  }
+  __syncthreads();
+  nA = ok ? tot.a : 0;
+  nB = ok ? tot.b : 0;
+  return ok;
+}
+
 // ------------------------------------------------------------------ k_stats
 // Persistent grid; wavefront gw takes units gw, gw + W, ...  The rows come
-// from two lists, rowlist (rowcount entries) then rowlist_b (rowcount_b
-// entries, may be absent), in that order.  The descriptor of the next unit is
-// fetched while the current one streams.
+// from the two lists, the first one then the second: from rowlist / rowlist_b
+// (written by k_plan), or, when a.plan_in_kernel, from the row table every
+// workgroup builds in LDS (dynamic shared memory of plan_lds_bytes(B, K)).
+// The descriptor of the next unit is fetched while the current one streams.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_stats(Args a) {
   using Elem = typename L::Elem;
+  extern __shared__ uint32_t row_table[];
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int W = gridDim.x * kWavesPerBlock;
-  const int nA = *a.rowcount;
-  const int nB = a.rowcount_b ? *a.rowcount_b : 0;
+  int nA, nB;
+  if (a.plan_in_kernel) {
+    plan_block(a, row_table, blockIdx.x == 0, nA, nB);
+  } else {
+    nA = *a.rowcount;
+    nB = a.rowcount_b ? *a.rowcount_b : 0;
+  }
   const int n_units = (nA + nB) * a.nseg;
-  auto desc_of = [&](int ri) { return ri < nA ? a.rowlist[ri] : a.rowlist_b[ri - nA]; };
+  auto desc_of = [&](int ri) -> uint32_t {
+    if (a.plan_in_kernel) return row_table[ri];
+    return ri < nA ? a.rowlist[ri] : a.rowlist_b[ri - nA];
+  };
   const Elem* tgt = static_cast<const Elem*>(a.target);
   const Elem* drf = static_cast<const Elem*>(a.draft);
   uint32_t next = (gw < n_units) ? desc_of(gw / a.nseg) : 0u;

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_tree_plan(Args a) {
     h->error = bad ? 1 : 0;
     h->n_rows = bad ? 0 : a.K;
     h->n_units = 0;
-    h->n_resid = 0;
+    h->n_stoch = 0;
     h->n_alive3[0] = (rounds && !bad) ? s_na : 0;   // (list order is free)
     h->n_rows3[0] = (rounds && !bad) ? s_na : 0;
     h->n_alive3[1] = 0;

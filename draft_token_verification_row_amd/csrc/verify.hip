@@ -50,16 +50,11 @@ namespace {
 
 // ------------------------------------------------------------------ k_plan
 
-// One workgroup: exclusive scan of k_b -> request offsets and records, and
-// the two lists of rows k_stats streams, 1024 requests per pass (wave
-// shuffles + one LDS step).  The second list holds the position-0 (target,
-// draft) pair of every stochastic request with k_b >= 1; k_stats reads it
-// last.  About half of all cuts fall at position 0, and the residual sweep
-// re-reads exactly the rejected pair, so reading those pairs last leaves the
-// most likely re-reads in the last-level cache (MALL) when the sweep runs.
-// The first list holds every other row: all target rows of greedy requests,
-// target rows 1..k_b and draft rows 1..k_b-1 of stochastic requests (target
-// row 0 when k_b = 0).
+// One workgroup: the plan of a call too large for k_stats to plan in LDS
+// (plan_fits_lds): exclusive scan of k_b -> request offsets and
+// records, the list of stochastic requests, and the two row lists k_stats
+// streams (row_counts, row_in_first, row_in_second), 1024 requests per pass
+// (wave shuffles + one LDS step).
 __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   constexpr int kPlanWaves = kPlanThreads / kWave;
   __shared__ long long s_w0[kPlanWaves];
@@ -70,34 +65,33 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
   if (tid == 0) s_bad = 0;
   __syncthreads();
   const long long TB = (long long)a.K + a.B;
-  long long carry_k = 0, carry_a = 0, carry_b = 0;
+  long long carry_k = 0, carry_a = 0, carry_b = 0, carry_s = 0;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
-    long long k = 0;
-    int g = 1;
+    int k = 0;
+    bool g = true;
     if (b < a.B) {
-      int kk = a.num_draft[b];
-      if (kk < 0 || kk > a.K) {
+      k = a.num_draft[b];
+      if (k < 0 || k > a.K) {
         s_bad = 1;
-        kk = 0;
+        k = 0;
       }
-      k = kk;
-      g = a.force_greedy ? 1 : (a.gmask ? (a.gmask[b] != 0) : 0);
+      g = a.force_greedy ? true : (a.gmask ? (a.gmask[b] != 0) : false);
     }
-    const bool pair0 = SV_MALL_ORDER && b < a.B && !g && k >= 1;
-    const long long cA = b >= a.B ? 0 : (g ? k + 1 : (pair0 ? 2 * k - 1 : 2 * k + 1));
-    const long long cB = pair0 ? 2 : 0;
+    int cA = 0, cB = 0;
+    if (b < a.B) row_counts(k, g, cA, cB);
     const Scan2 sc = block_scan2(k, cA, s_w0, s_w1, s_tot);
     __syncthreads();
-    const Scan2 sb = block_scan2(cB, 0, s_w0, s_w1, s_tot);
+    const Scan2 sb = block_scan2(cB, (b < a.B && !g) ? 1 : 0, s_w0, s_w1, s_tot);
     const long long off = carry_k + sc.ex0;
     const long long aoff = carry_a + sc.ex1;
     const long long boff = carry_b + sb.ex0;
+    const long long soff = carry_s + sb.ex1;
     if (b < a.B) {
       ReqInfo r;
       r.off = (int)off;
-      r.k = (int)k;
-      r.greedy = g;
+      r.k = k;
+      r.greedy = g ? 1 : 0;
       r.a = 0;
       r.kind = KIND_NONE;
       r.y = -1;
@@ -107,22 +101,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
       r.pad0 = r.pad1 = 0;
       r.Sp = r.Sq = 0.0;
       a.ws.req[b] = r;
-      const long long cap_a = 2ll * a.K + a.B;      // bounds: off may be wrong if num_draft is
-      const uint32_t gbit = g ? kGreedyBit : 0u;
-      long long j = aoff;
-      for (long long i = pair0 ? 1 : 0; i <= k; ++i, ++j)       // target rows
-        if (j < cap_a && off + b + i < TB) a.ws.rowdesc[j] = (uint32_t)(off + b + i) | gbit;
-      if (!g)
-        for (long long i = pair0 ? 1 : 0; i < k; ++i, ++j)      // draft rows
-          if (j < cap_a && off + i < a.K) a.ws.rowdesc[j] = (uint32_t)(off + i) | kDraftBit;
-      if (pair0 && boff + 1 < 2ll * a.B && off + b < TB && off < a.K) {
-        a.ws.rowdesc_b[boff] = (uint32_t)(off + b);
-        a.ws.rowdesc_b[boff + 1] = (uint32_t)off | kDraftBit;
-      }
+      if (!g && soff < a.B) a.ws.stoch_list[soff] = b;
+      // (offsets are wrong when num_draft is inconsistent: the call is then
+      // reported as an error, and every write stays inside its list)
+      if (off + b + k < TB)
+        for (int j = 0; j < cA; ++j)
+          if (aoff + j < 2ll * a.K + a.B) a.ws.rowdesc[aoff + j] = row_in_first(b, j, (int)off, k, g);
+      if (off < a.K)
+        for (int j = 0; j < cB; ++j)
+          if (boff + j < 2ll * a.B) a.ws.rowdesc_b[boff + j] = row_in_second(b, j, (int)off);
     }
     carry_k += sc.tot0;
     carry_a += sc.tot1;
     carry_b += sb.tot0;
+    carry_s += sb.tot1;
     __syncthreads();
   }
   if (tid == 0) {
@@ -131,8 +123,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(Args a) {
     h->error = bad ? 1 : 0;
     h->n_rows = bad ? 0 : (int)carry_a;
     h->n_rows_b = bad ? 0 : (int)carry_b;
+    h->n_stoch = bad ? 0 : (int)carry_s;
     h->n_units = 0;
-    h->n_resid = 0;
   }
 }
 
@@ -208,16 +200,20 @@ __device__ __forceinline__ float logit_at(const void* base, int64_t row, int64_t
   return D::one(static_cast<const typename D::Elem*>(base) + row * ld + v);
 }
 
-// ------------------------------------------------------------------ k_decide
-// One wavefront per request.  Positions are taken 32 at a time: lane l < 32
-// combines the target row of position base+l, lane l+32 the draft row of the
-// same position, so every row of a request is combined in parallel.
-// Decision of every position of request b by one wavefront (all rows' partials
-// are in the workspace).  queue: list the request for k_resid when it needs a
-// residual sweep (the single-launch path sweeps it in the same workgroup).
+// ------------------------------------------------------------------ decisions
+// Decision of every position of request b by one wavefront, from the row
+// partials in the workspace and R, the request's plan record (offset, k_b,
+// greedy).  Positions are taken 32 at a time: lane l < 32 combines the target
+// row of position base+l, lane l+32 the draft row of the same position, so
+// every row of a request is combined in parallel.  Returns the decision record
+// (cut, final row, and for stochastic requests the statistics of the rows the
+// draw needs), the same in every lane.  write: also write the request's
+// outputs (accepted length, kept drafts, greedy target token, p(y), q(y), -1
+// slots) and its record; several wavefronts may compute the same decision, and
+// exactly one of them writes.
 template <class D>
-__device__ __forceinline__ void decide_request(const Args& a, int b, int lane, bool queue) {
-  const ReqInfo R = a.ws.req[b];
+__device__ __forceinline__ ReqInfo decide_request(const Args& a, int b, int lane, bool write,
+                                                  const ReqInfo& R) {
   const int k = R.k;
   const int trow0 = R.off + b;
   const int drow0 = R.off;
@@ -269,19 +265,17 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
       if (g) {
         rej = (y != amax);
       } else if (!yok) {
-        invalid = true;
-        if (a.p_out) a.p_out[drow0 + i] = -1.f;
-        if (a.q_out) a.q_out[drow0 + i] = -1.f;
+        invalid = true;  // every output of the request becomes -1 below
       } else if (!pos_ok) {
-        rej = true;      // the request is reported invalid (this position is tested)
-        if (a.p_out) a.p_out[drow0 + i] = -1.f;
-        if (a.q_out) a.q_out[drow0 + i] = -1.f;
+        rej = true;      // a row without mass: -1 here (the request is invalid if tested)
+        if (write && a.p_out) a.p_out[drow0 + i] = -1.f;
+        if (write && a.q_out) a.q_out[drow0 + i] = -1.f;
       } else {
         const double py = exp2(((double)zy - (double)M) * a.c64) / S;
         const double qy = exp2(((double)dy - (double)Mq) * a.c64) / Sq;
         rej = !((double)a.u_accept[drow0 + i] * qy < py);
-        if (a.p_out) a.p_out[drow0 + i] = (float)py;
-        if (a.q_out) a.q_out[drow0 + i] = (float)qy;
+        if (write && a.p_out) a.p_out[drow0 + i] = (float)py;
+        if (write && a.q_out) a.q_out[drow0 + i] = (float)qy;
       }
     }
     const unsigned long long rm = __ballot(rej);
@@ -307,6 +301,43 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
     }
     if (g && found) break;
   }
+  ReqInfo W = R;
+  if (__any(invalid) || no_mass) {
+    W.kind = KIND_INVALID;
+    if (write) {
+      for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
+      for (int i = lane; i < k; i += kWave) {
+        if (a.p_out) a.p_out[drow0 + i] = -1.f;
+        if (a.q_out) a.q_out[drow0 + i] = -1.f;
+      }
+      if (lane == 0) {
+        a.acc_len[b] = -1;
+        if (a.resid_out) a.resid_out[b] = -1.f;
+        a.ws.req[b] = W;
+      }
+    }
+    return W;
+  }
+  W.a = A;
+  W.trow = trow0 + A;
+  if (g) {
+    W.kind = KIND_NONE;
+  } else {
+    W.Mp = MpA;
+    W.Sp = SpA;
+    if (A < k) {
+      W.kind = KIND_RESID;
+      W.drow = drow0 + A;
+      W.y = a.tokens[drow0 + A];
+      W.Mq = MqA;
+      W.Sq = SqA;
+    } else {
+      W.kind = KIND_BONUS;
+      W.drow = -1;
+      W.y = -1;
+    }
+  }
+  if (!write) return W;
   if (g) {
     // no probabilities for greedy rows: every position, also those after the
     // cut that the loop above never reached
@@ -314,19 +345,6 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
       if (a.p_out) a.p_out[drow0 + i] = -1.f;
       if (a.q_out) a.q_out[drow0 + i] = -1.f;
     }
-  }
-  if (__any(invalid) || no_mass) {
-    for (int i = lane; i <= k; i += kWave) a.out[trow0 + i] = -1;
-    for (int i = lane; i < k; i += kWave) {
-      if (a.p_out) a.p_out[drow0 + i] = -1.f;
-      if (a.q_out) a.q_out[drow0 + i] = -1.f;
-    }
-    if (lane == 0) {
-      a.acc_len[b] = -1;
-      if (a.resid_out) a.resid_out[b] = -1.f;
-      a.ws.req[b].kind = KIND_INVALID;
-    }
-    return;
   }
   const int final_tok = g ? (amaxA == INT_MAX ? -1 : amaxA) : -1;
   for (int i = lane; i <= k; i += kWave) {
@@ -338,56 +356,24 @@ __device__ __forceinline__ void decide_request(const Args& a, int b, int lane, b
   if (lane == 0) {
     a.acc_len[b] = A;
     if (a.resid_out) a.resid_out[b] = -1.f;
-    ReqInfo W = R;
-    W.a = A;
-    W.trow = trow0 + A;
-    if (g) {
-      W.kind = KIND_NONE;
-    } else {
-      W.Mp = MpA;
-      W.Sp = SpA;
-      if (A < k) {
-        W.kind = KIND_RESID;
-        W.drow = drow0 + A;
-        W.y = a.tokens[drow0 + A];
-        W.Mq = MqA;
-        W.Sq = SqA;
-        if (queue) {
-          const int j = atomicAdd(&a.ws.hdr->n_resid, 1);
-          a.ws.resid_list[j] = b;
-        }
-      } else {
-        W.kind = KIND_BONUS;
-        W.drow = -1;
-        W.y = -1;
-      }
-    }
     a.ws.req[b] = W;
   }
+  return W;
 }
 
 
-template <class D>
-__global__ __launch_bounds__(kBlock) void k_decide(Args a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int b = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (a.ws.hdr->error) {
-    // inconsistent num_draft: every output slot becomes -1
-    const long long gt = (long long)blockIdx.x * kBlock + threadIdx.x;
-    const long long gs = (long long)gridDim.x * kBlock;
-    for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
-    for (long long i = gt; i < a.B; i += gs) {
-      a.acc_len[i] = -1;
-      if (a.resid_out) a.resid_out[i] = -1.f;
-    }
-    for (long long i = gt; i < a.K; i += gs) {
-      if (a.p_out) a.p_out[i] = -1.f;
-      if (a.q_out) a.q_out[i] = -1.f;
-    }
-    return;
+// Every output slot of a call whose num_draft is inconsistent becomes -1;
+// thread gt of gs threads in all takes its share.
+__device__ __forceinline__ void fill_error_outputs(const Args& a, long long gt, long long gs) {
+  for (long long i = gt; i < (long long)a.K + a.B; i += gs) a.out[i] = -1;
+  for (long long i = gt; i < a.B; i += gs) {
+    a.acc_len[i] = -1;
+    if (a.resid_out) a.resid_out[i] = -1.f;
   }
-  if (b >= a.B) return;
-  decide_request<D>(a, b, lane, true);
+  for (long long i = gt; i < a.K; i += gs) {
+    if (a.p_out) a.p_out[i] = -1.f;
+    if (a.q_out) a.q_out[i] = -1.f;
+  }
 }
 
 // ------------------------------------------------------------------ draw weights
@@ -525,20 +511,27 @@ __device__ __forceinline__ double resid_unit(const typename L::Elem* tp, const t
 }
 
 // ------------------------------------------------------------------ k_resid
-// Persistent grid; one wavefront per residual unit (rseg ids of one row pair).
+// Persistent grid over the residual units of the stochastic requests (nrseg
+// units of rseg ids of each request's rejected row pair; the list of
+// stochastic requests comes from the plan).  Each wavefront takes a
+// contiguous range of units, so its units mostly belong to one request, and
+// it decides that request itself (decide_request over the row partials of
+// k_stats) before sweeping: the decision needs no launch of its own.  The
+// wavefront whose range holds a request's unit 0 also writes the request's
+// outputs and record; a request cut at no position (bonus) or invalid has
+// nothing to sweep.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
   using Elem = typename L::Elem;
+  if (a.ws.hdr->error) return;          // k_finalize writes the -1 outputs
   const int lane = threadIdx.x & (kWave - 1);
   const int gw = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  // each wavefront takes a contiguous range of units, so consecutive units
-  // mostly share a request and its record is fetched once
   const int W = gridDim.x * kWavesPerBlock;
-  const long long n_units = (long long)a.ws.hdr->n_resid * a.nrseg;
+  const long long n_units = (long long)a.ws.hdr->n_stoch * a.nrseg;
   const int u_begin = (int)(n_units * gw / W);
   const int u_end = (int)(n_units * (gw + 1) / W);
   int cur = -1, b = 0;
-  ReqInfo R;
+  ReqInfo D;
   ResidW fw;
   const Elem* tp = nullptr;
   const Elem* dp = nullptr;
@@ -547,15 +540,19 @@ __global__ __launch_bounds__(kBlock) void k_resid(Args a) {
     const int seg = u - j * a.nrseg;
     if (j != cur) {
       cur = j;
-      b = a.ws.resid_list[j];
-      R = a.ws.req[b];
-      fw = resid_weights(R, a);
-      tp = static_cast<const Elem*>(a.target) + (int64_t)R.trow * a.tld;
-      dp = static_cast<const Elem*>(a.draft) + (int64_t)R.drow * a.dld;
+      b = a.ws.stoch_list[j];
+      const ReqInfo R = a.ws.req[b];
+      D = decide_request<L>(a, b, lane, (long long)j * a.nrseg >= u_begin, R);
+      if (D.kind == KIND_RESID) {
+        fw = resid_weights(D, a);
+        tp = static_cast<const Elem*>(a.target) + (int64_t)D.trow * a.tld;
+        dp = static_cast<const Elem*>(a.draft) + (int64_t)D.drow * a.dld;
+      }
     }
+    if (D.kind != KIND_RESID) continue;
     const int s0 = seg * a.rseg;
     const int s1 = min(s0 + a.rseg, a.V);
-    const double tot = resid_unit<L, kResidUnroll>(tp, dp, fw, R.y, s0, s1, lane);
+    const double tot = resid_unit<L, kResidUnroll>(tp, dp, fw, D.y, s0, s1, lane);
     if (lane == 0) a.ws.rp[(int64_t)b * a.nrseg + seg] = tot;
   }
 }
@@ -1056,15 +1053,26 @@ __device__ __forceinline__ DrawInputs draw_inputs(const Args& a, int b) {
   const int lane = threadIdx.x & (kWave - 1);
   d.rp = (threadIdx.x < kWave && lane < a.nrseg) ? a.ws.rp[(int64_t)b * a.nrseg + lane] : 0.0;
   d.R = a.ws.req[b];
-  d.w = (double)a.u_final[b];
+  d.w = a.u_final ? (double)a.u_final[b] : 0.0;
   return d;
 }
 
+// One workgroup per request: the decision of a greedy request (wavefront
+// 0), or the correction / bonus draw of a stochastic one; when num_draft is
+// inconsistent, every output slot becomes -1 instead.
 template <class L>
 __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
   __shared__ FinalizeShared sh;
   const DrawInputs d = draw_inputs(a, blockIdx.x);
-  if (a.ws.hdr->error) return;
+  if (a.ws.hdr->error) {
+    fill_error_outputs(a, (long long)blockIdx.x * kBlock + threadIdx.x,
+                       (long long)gridDim.x * kBlock);
+    return;
+  }
+  if (d.R.greedy) {
+    if (threadIdx.x < kWave) decide_request<L>(a, blockIdx.x, threadIdx.x, true, d.R);
+    return;
+  }
   finalize_request<L, true>(a, blockIdx.x, d.R, d.w, d.rp, sh);
 }
 
@@ -1170,7 +1178,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
       softmax_unit<L, kFusedUnroll>(base, s0, s1, lane, a, out);
   }
   __syncthreads();
-  if (wv == 0) decide_request<L>(a, b, lane, false);
+  if (wv == 0) decide_request<L>(a, b, lane, true, a.ws.req[b]);
   __syncthreads();
   const ReqInfo R = a.ws.req[b];
   if (R.kind == KIND_RESID) {
@@ -1279,7 +1287,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
     const bool bad = s_bad != 0 || carry_k != a.K;
     Header* h = a.ws.hdr;
     h->error = bad ? 1 : 0;
-    h->n_resid = 0;
+    h->n_stoch = 0;
     h->n_rows3[0] = bad ? 0 : (int)carry_r;
     h->n_res3[0] = 0;
     h->n_alive3[0] = bad ? 0 : a.B;
@@ -1604,17 +1612,20 @@ void launch_all(const Args& a, hipStream_t st, int dev, bool sample) {
   const long long units_resid = (long long)a.B * a.nrseg;
   const long long cap_s = cus * resident_blocks(occ_stats, k_stats<L>, dev);
   const int grid_stats = (int)std::max(1ll, std::min(cap_s, (units_stats + kWavesPerBlock - 1) / kWavesPerBlock));
-  k_plan<<<1, kPlanThreads, 0, st>>>(a);
+  // small enough calls are planned by k_stats itself (the row table in LDS)
+  Args sa = a;
+  sa.plan_in_kernel = plan_fits_lds(a.B, a.K) ? 1 : 0;
+  const size_t lds = sa.plan_in_kernel ? plan_lds_bytes(a.B, a.K) : 0;
+  if (!sa.plan_in_kernel) k_plan<<<1, kPlanThreads, 0, st>>>(a);
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
-  k_stats<L><<<grid_stats, kBlock, 0, st>>>(a);
+  k_stats<L><<<grid_stats, kBlock, lds, st>>>(sa);
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
-  k_decide<L><<<(a.B + kWavesPerBlock - 1) / kWavesPerBlock, kBlock, 0, st>>>(a);
   if (sample) {
     const long long cap_r = cus * resident_blocks(occ_resid, k_resid<L>, dev);
     const int grid_resid = (int)std::max(1ll, std::min(cap_r, (units_resid + kWavesPerBlock - 1) / kWavesPerBlock));
     k_resid<L><<<grid_resid, kBlock, 0, st>>>(a);
-    k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
   }
+  k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
 }
 
 template <class L>
@@ -1721,7 +1732,7 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
   a.ws.req = reinterpret_cast<ReqInfo*>(wb + z.off_req);
   a.ws.rowdesc = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc);
   a.ws.rowdesc_b = reinterpret_cast<uint32_t*>(wb + z.off_rowdesc_b);
-  a.ws.resid_list = reinterpret_cast<int*>(wb + z.off_resid);
+  a.ws.stoch_list = reinterpret_cast<int*>(wb + z.off_resid);
   a.ws.pt = reinterpret_cast<Partial*>(wb + z.off_pt);
   a.ws.pd = reinterpret_cast<Partial*>(wb + z.off_pd);
   a.ws.rp = reinterpret_cast<double*>(wb + z.off_rp);
