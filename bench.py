@@ -424,6 +424,34 @@ def bench_adaptive(args, sv, torch):
     print(json.dumps(res), flush=True)
 
 
+def read_probe(mib: int, steps: int, warmup: int):
+    """The plain streaming read of the library (the access pattern of the
+    row-statistics kernel without its arithmetic) over mib MiB: the read
+    bandwidth ceiling, from the events the library records around its launch."""
+    import torch
+    import draft_token_verification_row_amd as sv
+    src = torch.randn(mib * (1 << 20) // 4, device="cuda:0")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda:0")
+    for _ in range(warmup):
+        sv.spec_verify_read_probe(src, sink)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    eb, ee = hip.create(steps), hip.create(steps)
+    for i in range(steps):
+        sv.spec_verify_set_profile_events(eb[i], ee[i])
+        sv.spec_verify_read_probe(src, sink)
+    torch.cuda.synchronize()
+    sv.spec_verify_set_profile_events(None, None)
+    ms = np.array([hip.elapsed_ms(eb[i], ee[i]) for i in range(steps)])
+    hip.destroy(eb + ee)
+    nbytes = src.numel() * 4
+    print(json.dumps({"read_probe_mib": mib, "steps": steps, "bytes": nbytes,
+                      "mean_us": float(ms.mean()) * 1e3, "median_us": float(np.median(ms)) * 1e3,
+                      "gbs_mean": nbytes / (ms.mean() / 1e3) / 1e9,
+                      "gbs_median": nbytes / (np.median(ms) / 1e3) / 1e9,
+                      "frac_of_8TBs": nbytes / (np.median(ms) / 1e3) / 1e9 / PEAK_HBM_GBS}), flush=True)
+
+
 def copy_probe(mib: int, steps: int):
     """A plain copy kernel of known size: reads and writes mib MiB per launch."""
     import torch
@@ -463,9 +491,13 @@ def main():
     ap.add_argument("--shards", type=int, default=1, metavar="G")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead: run `steps` plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="instead: time the library's plain streaming read over MIB MiB")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe, args.steps)
+    if args.read_probe:
+        return read_probe(args.read_probe, args.steps, args.warmup)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

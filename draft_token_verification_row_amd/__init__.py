@@ -31,7 +31,8 @@ EXPORTED = ("spec_verify_workspace_bytes", "spec_verify_status_string",
             "spec_verify_set_profile_events", "spec_verify_tree_workspace_bytes",
             "spec_verify_tree_greedy", "spec_verify_tree_greedy_early_exit",
             "spec_verify_adaptive_length", "spec_verify_gather_rows",
-            "spec_verify_set_launch_plan", "spec_verify_sample_noalloc")
+            "spec_verify_set_launch_plan", "spec_verify_sample_noalloc",
+            "spec_verify_read_probe")
 
 # SPEC_VERIFY_NOALLOC_MAX_BYTES of the C header: the largest workspace that
 # spec_verify_sample_noalloc serves from its static device array.
@@ -88,6 +89,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_sample_noalloc.argtypes = [ctypes.POINTER(SvBatch), ctypes.c_float, vp, vp, vp,
                                                vp, vp, vp, vp, vp, vp]
     lib.spec_verify_sample_noalloc.restype = i32
+    lib.spec_verify_read_probe.argtypes = [vp, sz, vp, vp]
+    lib.spec_verify_read_probe.restype = i32
     lib.spec_verify_accept_stats.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.spec_verify_accept_stats.restype = i32
     lib.spec_verify_tree_workspace_bytes.argtypes = [i32, i32, i32]
@@ -169,6 +172,14 @@ def spec_verify_set_launch_plan(plan: int) -> None:
 
 def spec_verify_set_profile_events(ev_begin: Optional[int], ev_end: Optional[int]) -> int:
     return int(lib().spec_verify_set_profile_events(ev_begin, ev_end))
+
+
+def spec_verify_read_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Plain streaming read of src (diagnostic: the read-bandwidth ceiling)."""
+    st = lib().spec_verify_read_probe(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                      _stream_handle(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st)
 
 
 def make_batch_struct(target: torch.Tensor, draft: Optional[torch.Tensor],

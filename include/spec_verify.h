@@ -322,6 +322,15 @@ int32_t spec_verify_sample_noalloc(const sv_batch_t* batch, float temperature,
  * the same bits.  Thread-local; SV_ERR_INVALID_ARG for other values. */
 int32_t spec_verify_set_launch_plan(int32_t plan);
 
+/* Diagnostic: a plain streaming read of `bytes` (a multiple of 16) at src
+ * (16-byte aligned) with the access pattern of the row-statistics kernel (one
+ * wavefront per 32 KiB unit, persistent grid, 16-byte nontemporal loads) and
+ * no arithmetic on the data: the read bandwidth the streaming kernels are
+ * measured against.  sink: device buffer of 64 uint32 that receives a store
+ * only if the data folds to one fixed value.  Honours
+ * spec_verify_set_profile_events. */
+int32_t spec_verify_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Diagnostics for measurement tools.  When both are non-NULL (hipEvent_t
  * handles), later calls made from the calling thread record ev_begin just
  * before and ev_end just after the row-statistics kernel (for the early-exit

@@ -293,3 +293,11 @@ def test_launch_plan_values(sv):
         assert sv.lib().spec_verify_set_launch_plan(bad) == sv.SV_ERR_INVALID_ARG
     for ok in (1, 2, 0):
         assert sv.lib().spec_verify_set_launch_plan(ok) == sv.SV_OK
+
+
+def test_read_probe_rejects_bad_arguments(sv):
+    f = sv.lib().spec_verify_read_probe
+    assert f(None, 16, 8, None) == sv.SV_ERR_INVALID_ARG          # no source
+    assert f(16, 16, None, None) == sv.SV_ERR_INVALID_ARG          # no sink
+    assert f(16, 24, 8, None) == sv.SV_ERR_INVALID_ARG             # not whole 16-byte chunks
+    assert f(8, 16, 8, None) == sv.SV_ERR_INVALID_ARG              # misaligned source
