@@ -41,6 +41,10 @@ SMALL = [
     ("c3_vocab_1", 3, dict(B=4, V=1, k=2)),
     ("c5_many_requests", 5, dict(B=2100, V=300)),
     ("c2_greedy_odd_V", 2, dict(B=40, V=33333)),
+    # more rows than k_stats plans in LDS (2K + B > 6144 with B <= 2048): the
+    # separate plan kernel writes the row lists
+    ("c5_rows_beyond_lds_plan", 5, dict(B=600, V=3001, k=7)),
+    ("c3_greedy_free_rows_beyond_lds_plan", 3, dict(B=400, V=2000, k=8)),
 ]
 
 
