@@ -245,6 +245,25 @@ def pin_special_cases(vm):
     assert len(outs) == 2
 
 
+def pin_temperature_reading(vm):
+    """Reading R1: the kernels take the temperature as an fp32 value, so an
+    fp64 T given to the oracle acts as fp32(T): p(y) and q(y) equal scipy's
+    softmax of z / fp32(T), which differs measurably from z / T here."""
+    rng = np.random.default_rng(8)
+    V = 50
+    z, d = _rows(rng, V, 2, sigma=3.0)
+    for T in (0.7, 0.3, 1.3):
+        T32 = float(np.float32(T))
+        r = _run(vm, z, d, [3, 5], False, T, [0.999999, 0.999999], 0.5)
+        for i, y in ((0, 3),):
+            want_p = scipy.special.softmax(z[i] / T32)[y]
+            want_q = scipy.special.softmax(d[i] / T32)[y]
+            other = scipy.special.softmax(z[i] / T)[y]
+            assert abs(want_p - other) > 1e-11 * want_p, T      # the two readings differ
+            assert abs(r["p_y"][i] - want_p) <= 1e-13 * want_p, (T, r["p_y"][i], want_p)
+            assert abs(r["q_y"][i] - want_q) <= 1e-13 * want_q, (T, r["q_y"][i], want_q)
+
+
 def pin_greedy_invariants(vm, n_req: int = 300, V: int = 64, k: int = 4, seed: int = 5):
     """On random rows with many exact ties: every kept draft attains its row's
     maximum and no lower id does; the token at the cut attains the maximum with
@@ -403,7 +422,8 @@ def pin_early_exit_form(vm, n_batches: int = 6, seed: int = 31):
 
 ALL_PINS = [pin_abr_example, pin_weather_example, pin_t1_t4_round, pin_greedy_ties,
             pin_exact_distribution_quadrature, pin_special_cases, pin_greedy_invariants,
-            pin_packed_batch, pin_decision_margins, pin_early_exit_form]
+            pin_packed_batch, pin_decision_margins, pin_early_exit_form,
+            pin_temperature_reading]
 
 
 # ---------------------------------------------------------------- acceptance statistics

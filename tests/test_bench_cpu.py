@@ -42,3 +42,18 @@ def test_early_exit_rows_between_exact_and_twice_exact():
         exact = int((acc + 1).sum() + np.minimum(acc + 1, k)[st].sum())
         full = int((k + 1).sum() + k[st].sum())
         assert exact <= got <= min(full, 2 * exact)
+
+
+def test_c_oracle_baseline_helpers():
+    """The C oracle timing leg of the CPU baseline: both forms, one and several
+    threads, and its agreement with the NumPy oracle on the same batch."""
+    import synth
+    b = synth.make_batch(5, "cpu", B=20, V=3001)
+    res, times = bench.run_c_oracle_timed(b, 3)
+    assert set(times) == {("all_rows", 1), ("all_rows", 3), ("early_exit", 1), ("early_exit", 3)}
+    assert all(t > 0 for t in times.values())
+    ref, _ = bench.run_oracle_timed(bench.oracle_inputs(b), 2, False)
+    assert bench.oracles_agree(b, res, ref)
+    bad = dict(res, out_tokens=res["out_tokens"].copy())
+    bad["out_tokens"][0] += 1
+    assert not bench.oracles_agree(b, bad, ref)

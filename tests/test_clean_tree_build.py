@@ -1,6 +1,7 @@
 """A clean copy of the tracked sources (no built library) imports the package,
 reports the missing library loudly on first use, and builds it with
-__graft_entry__.build() (CPU only: hipcc cross-compiles for gfx950 here)."""
+__graft_entry__.build(), which also compiles the C oracle (CPU only: hipcc
+cross-compiles for gfx950 here)."""
 import os
 import shutil
 import subprocess
@@ -9,7 +10,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = ("__graft_entry__.py", "include", "draft_token_verification_row_amd", "synth")
+SOURCES = ("__graft_entry__.py", "include", "draft_token_verification_row_amd", "synth", "oracle")
 
 
 def _copy_sources(dst):
@@ -46,4 +47,5 @@ def test_build_from_a_tree_without_the_library(tmp_path):
              "print('bytes', sv.spec_verify_workspace_bytes(4, 8, 1000))\n", tmp_path)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
     assert so.exists()
+    assert (tmp_path / "oracle" / "liboracle_verify.so").exists()     # the C oracle, built too
     assert "bytes " in r.stdout and int(r.stdout.split("bytes ")[-1]) > 0

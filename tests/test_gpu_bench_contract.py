@@ -34,6 +34,8 @@ def test_default_bench_line():
     assert cb["variants"] and all(v["value"] > 0 for v in cb["variants"].values())
     par = line["parity"]
     assert par["requests"] == 512 and par["mismatches"] == 0, par
+    assert par["c_oracle_agrees"] is True, par        # the two oracles on the full batch
+    assert any(k.startswith("c_all_rows") for k in cb["variants"]), cb["variants"]
     cf = line["configs"]
     assert len(cf) == 5 and "ragged_mixed_v262144" in cf
     for name, c in cf.items():

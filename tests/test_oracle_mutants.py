@@ -116,6 +116,7 @@ MUTANTS = {
     "cdf_left_side": ("inverse_cdf", _cdf_left),
     "cdf_descending": ("inverse_cdf", _cdf_descending),
     "cdf_unscaled_threshold": ("inverse_cdf", _cdf_unscaled),
+    "temperature_not_widened": ("widen_temperature", lambda T: float(T)),
     "softmax_ignores_T": ("tempered_softmax", lambda z, T: _orig_softmax(z, 1.0)),
     "softmax_times_T": ("tempered_softmax", lambda z, T: _orig_softmax(np.asarray(z) * T * T, T)),
     "argmax_highest_id": ("lowest_argmax",

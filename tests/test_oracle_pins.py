@@ -45,6 +45,10 @@ def test_decision_margins():
     pins.pin_decision_margins(vm)
 
 
+def test_temperature_reading():
+    pins.pin_temperature_reading(vm)
+
+
 def test_early_exit_form():
     pins.pin_early_exit_form(vm)
 
