@@ -1077,20 +1077,27 @@ __global__ __launch_bounds__(kBlock) void k_finalize(Args a) {
 }
 
 // ------------------------------------------------------------------ single-launch path
-// Small batches: one workgroup of kFusedThreads threads per request runs the
-// whole step (offsets, row statistics, decisions, residual sweep, draw) with
-// only block barriers between the phases, so a call is one launch instead of
-// five.  Every phase calls the same unit, combine, decide and draw code as the
-// multi-kernel path, so the results are the same bit for bit.
-constexpr int kFusedThreads = 1024;
-constexpr int kFusedWaves = kFusedThreads / kWave;
+// Small batches: one workgroup per request runs the whole step (offsets, row
+// statistics, decisions, residual sweep, draw) with only block barriers
+// between the phases, so a call is one launch instead of three.  Every phase
+// calls the same unit, combine, decide and draw code as the multi-kernel
+// path, so the results are the same bit for bit, for any workgroup size.
+// Workgroups of 1024 threads for fp32 logits; 512 for bf16, whose decision
+// and draw code needs more than the 128 registers a 1024-thread workgroup
+// leaves each lane (it spilled there, and the 512-thread workgroup measured
+// faster on the greedy V = 32000 batch).
+template <class L>
+constexpr int fused_threads() { return sizeof(typename L::Elem) == 2 ? 512 : 1024; }
+constexpr int kFusedMaxWaves = 1024 / kWave;
 constexpr int kFusedUnroll = 4;
 constexpr int kFusedResidUnroll = 2;
 
 template <class L>
-__global__ __launch_bounds__(kFusedThreads) void k_fused(Args a) {
+__global__ __launch_bounds__(fused_threads<L>()) void k_fused(Args a) {
+  constexpr int kFusedThreads = fused_threads<L>();
+  constexpr int kFusedWaves = kFusedThreads / kWave;
   __shared__ FinalizeShared sh;
-  __shared__ long long s_pre[kFusedWaves], s_tot[kFusedWaves];
+  __shared__ long long s_pre[kFusedMaxWaves], s_tot[kFusedMaxWaves];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -1599,7 +1606,7 @@ constexpr int kFusedMaxRequests = 2048;
 template <class L>
 void launch_fused(const Args& a, hipStream_t st) {
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_begin, st);
-  k_fused<L><<<a.B, kFusedThreads, 0, st>>>(a);
+  k_fused<L><<<a.B, fused_threads<L>(), 0, st>>>(a);
   if (g_ev_begin && g_ev_end) (void)hipEventRecord((hipEvent_t)g_ev_end, st);
 }
 
