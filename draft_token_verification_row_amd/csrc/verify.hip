@@ -8,25 +8,33 @@
 //
 // All-rows pipeline (spec_verify_greedy / spec_verify_sample; every launch on
 // the caller's stream, no host synchronisation):
-//   k_plan      one workgroup: exclusive scan of num_draft -> request offsets,
-//               compact list of logit rows to read (every target row, the draft
-//               rows of stochastic requests), unit count.
 //   k_stats     persistent grid, one wavefront per 32 KiB slice ("unit") of a
-//               row.  Streams the logits once from HBM with 16-byte loads and
-//               writes per-unit partials: online max and sum of exp((z-max)/T)
-//               for softmax rows, (max, lowest id) for greedy rows.  This is the
-//               HBM-bound kernel that carries almost all bytes.
-//   k_decide    one wavefront per request: combines the partials of each row,
-//               evaluates p(y_i), q(y_i) in fp64, runs the ratio test (stochastic)
-//               or argmax test (greedy) for every position, cuts at the first
-//               rejection, commits the kept drafts and the greedy target token,
-//               and queues a residual job for stochastic requests cut early.
-//   k_resid     persistent grid: second sweep of the one (target, draft) row pair
-//               of each queued request, per-unit sums of [p - q]_+.
-//   k_finalize  one workgroup per stochastic request: finds the unit holding
-//               the inverse-CDF crossing from the unit sums (bonus: from the
-//               k_stats partials, no re-read), rescans that unit only and writes
-//               the correction / bonus token.
+//               row.  Each workgroup first plans the call in LDS (exclusive
+//               scan of num_draft, the table of logit rows to read: every
+//               target row, the draft rows of stochastic requests); workgroup 0
+//               also writes the request records and the list of stochastic
+//               requests.  Then it streams the logits once from HBM with
+//               16-byte loads and writes per-unit partials: online max and sum
+//               of exp((z-max)/T) for softmax rows, (max, lowest id) for greedy
+//               rows.  This is the HBM-bound kernel that carries almost all
+//               bytes.  (k_plan writes the same plan to the workspace first
+//               when a call has more requests or rows than the LDS table holds.)
+//   k_resid     persistent grid over the residual units of the stochastic
+//               requests.  A wavefront first decides the request its units
+//               belong to (decide_request: combines the partials of each row,
+//               evaluates p(y_i), q(y_i) in fp64, runs the ratio tests left to
+//               right, cuts at the first rejection; the wavefront holding the
+//               request's first unit writes its outputs), then, if the request
+//               was cut by a rejection, sums [p - q]_+ over its units of the
+//               rejected (target, draft) row pair.
+//   k_finalize  one workgroup per request: the decision of a greedy request
+//               (the argmax tests and the target's token), or the draw of a
+//               stochastic one: finds the unit holding the inverse-CDF crossing
+//               from the unit sums (bonus: from the k_stats partials, no
+//               re-read), rescans that unit only, keeps the fp32 draw when its
+//               margin certifies it and otherwise redoes it in fp64.
+// Small calls run all of this in one launch instead (k_fused, one workgroup
+// per request).
 //
 // Early-exit pipeline (the *_early_exit entry points): k_plan_ee, then per
 // window of positions a k_round launch (row statistics of the window's rows
@@ -1309,7 +1317,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_ee(Args a) {
 // Decision of the positions [lo, hi) of request b (up to its cut) by one
 // wavefront, 32 positions at a time: lane l < 32 combines the target row of
 // position base + l and lane l + 32 its draft row, with the per-row combines
-// of k_decide, so both paths see the same statistics bit for bit.  A request
+// of decide_request, so both paths see the same statistics bit for bit.  A request
 // that keeps every position of the window lists the rows of [hi, nhi) for the
 // next round; a cut lists the request's residual sweep.
 template <class L>
@@ -1594,7 +1602,7 @@ bool compute_sizes(long long B, long long K, long long V, Sizes* z) {
 
 
 // Logit bytes up to which a batch runs as one launch (one workgroup per
-// request): below this the five-kernel path is bound by launch latency.
+// request): below this the multi-kernel path is bound by launch latency.
 constexpr long long kFusedMaxBytes = 48ll << 20;
 constexpr int kFusedMaxRequests = 2048;
 
