@@ -1680,11 +1680,11 @@ void launch_early_exit(const Args& a, hipStream_t st, int dev, bool sample) {
   if (sample) k_finalize<L><<<a.B, kBlock, 0, st>>>(a);
 }
 
-int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t* gmask,
-            const float* u_accept, const float* u_final, int32_t* acc_len, int32_t* out,
-            float* p_out, float* q_out, float* resid_out, void* ws, size_t ws_bytes,
-            void* stream, bool early_exit, int max_k) {
-  // ---- host-side checks: nothing below touches the GPU until they pass
+// Host-side checks of a verification call (everything but the workspace);
+// they touch no GPU state.  *z receives the workspace layout of the call.
+int32_t host_checks(const sv_batch_t* bt, bool sample, float temperature, const float* u_accept,
+                    const float* u_final, const int32_t* acc_len, const int32_t* out,
+                    bool early_exit, int max_k, Sizes* zp) {
   if (!bt) return SV_ERR_INVALID_ARG;
   if (early_exit && (max_k < 0 || max_k > kMaxEarlyExitRounds)) return SV_ERR_INVALID_ARG;
   const long long B = bt->B, K = bt->K, V = bt->V;
@@ -1708,8 +1708,24 @@ int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t*
     if (bt->draft_ld < V || bt->draft_ld > (1ll << 40)) return SV_ERR_INVALID_ARG;
     if ((uintptr_t)bt->draft % es != 0) return SV_ERR_INVALID_ARG;
   }
+  *zp = z;
+  return SV_OK;
+}
+
+int32_t run(const sv_batch_t* bt, bool sample, float temperature, const uint8_t* gmask,
+            const float* u_accept, const float* u_final, int32_t* acc_len, int32_t* out,
+            float* p_out, float* q_out, float* resid_out, void* ws, size_t ws_bytes,
+            void* stream, bool early_exit, int max_k) {
+  // ---- host-side checks: nothing below touches the GPU until they pass
+  Sizes z;
+  const int32_t chk = host_checks(bt, sample, temperature, u_accept, u_final, acc_len, out,
+                                  early_exit, max_k, &z);
+  if (chk != SV_OK) return chk;
   if (!ws) return SV_ERR_WORKSPACE;
   if (ws_bytes < z.total) return SV_ERR_WORKSPACE;
+  const long long B = bt->B, K = bt->K, V = bt->V;
+  const int es = bt->dtype == SV_F32 ? 4 : 2;
+  const bool need_draft = sample && K > 0;
 
   // ---- argument block
   const uintptr_t wb = align_up((uintptr_t)ws, 256);
@@ -1837,9 +1853,10 @@ extern "C" int32_t spec_verify_sample_noalloc(const sv_batch_t* batch, float tem
                                               const float* u_final, int32_t* accepted_len,
                                               int32_t* out_tokens, float* p_draft, float* q_draft,
                                               float* resid_mass, void* stream) {
-  if (!batch) return SV_ERR_INVALID_ARG;
   Sizes z;
-  if (!compute_sizes(batch->B, batch->K, batch->V, &z)) return SV_ERR_INVALID_ARG;
+  const int32_t chk = host_checks(batch, true, temperature, u_accept, u_final, accepted_len,
+                                  out_tokens, false, 0, &z);
+  if (chk != SV_OK) return chk;
   if (z.total > (size_t)SPEC_VERIFY_NOALLOC_MAX_BYTES) return SV_ERR_WORKSPACE;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;

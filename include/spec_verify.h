@@ -299,9 +299,12 @@ int32_t spec_verify_gather_rows(int32_t dtype, int32_t V, const void* src, int64
  * spec_verify_sample with the same arguments and results, minus the workspace,
  * which is a static device array of SPEC_VERIFY_NOALLOC_MAX_BYTES that the
  * library holds on every device it runs on until the process ends.  The call
- * allocates nothing and returns SV_ERR_WORKSPACE (launching and writing
- * nothing) when spec_verify_workspace_bytes(B, K, V) exceeds that size (for
- * example B = 2048 requests with 8 drafts each at V = 262144 fit).  Every call
+ * allocates nothing.  It runs the host checks of spec_verify_sample first, and
+ * returns SV_ERR_WORKSPACE when spec_verify_workspace_bytes(B, K, V) exceeds
+ * that size (for example B = 2048 requests with 8 drafts each at V = 262144
+ * fit); a call refused either way makes no HIP call and writes nothing.  The
+ * array's device address is looked up once per device, on the first call that
+ * passes those checks (SV_ERR_HIP if that fails).  Every call
  * on one device uses the same array, which keeps the last call's contents:
  * calls that overlap on one device (two streams, two host threads) race and
  * must be serialised by the caller.  Launch plan and results as for

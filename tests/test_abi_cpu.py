@@ -301,3 +301,26 @@ def test_read_probe_rejects_bad_arguments(sv):
     assert f(16, 16, None, None) == sv.SV_ERR_INVALID_ARG          # no sink
     assert f(16, 24, 8, None) == sv.SV_ERR_INVALID_ARG             # not whole 16-byte chunks
     assert f(8, 16, 8, None) == sv.SV_ERR_INVALID_ARG              # misaligned source
+
+
+def _noalloc(sv, bt, T=1.0, ua=FAKE, uf=FAKE, acc=FAKE, out=FAKE):
+    return sv.lib().spec_verify_sample_noalloc(ctypes.byref(bt), ctypes.c_float(T), None, ua, uf,
+                                              acc, out, None, None, None, None)
+
+
+def test_noalloc_host_validation(sv):
+    """The entry point that uses the library's static workspace runs the same
+    host checks as spec_verify_sample, and refuses a call whose workspace
+    would exceed its array, before any HIP call (so also without a GPU)."""
+    INV, UNS, WS = sv.SV_ERR_INVALID_ARG, sv.SV_ERR_UNSUPPORTED, sv.SV_ERR_WORKSPACE
+    assert sv.lib().spec_verify_sample_noalloc(None, ctypes.c_float(1.0), None, FAKE, FAKE, FAKE,
+                                              FAKE, None, None, None, None) == INV
+    assert _noalloc(sv, _batch(sv, B=0)) == INV
+    assert _noalloc(sv, _batch(sv, dtype=7)) == UNS
+    assert _noalloc(sv, _batch(sv, draft=None)) == INV
+    assert _noalloc(sv, _batch(sv), T=0.0) == INV
+    assert _noalloc(sv, _batch(sv), uf=None) == INV
+    assert _noalloc(sv, _batch(sv), out=None) == INV
+    big = dict(B=4096, K=65536, V=262144, target_ld=262144, draft_ld=262144)
+    assert sv.spec_verify_workspace_bytes(4096, 65536, 262144) > sv.NOALLOC_MAX_BYTES
+    assert _noalloc(sv, _batch(sv, **big)) == WS
