@@ -586,7 +586,11 @@ struct UnitMass {
   __device__ __forceinline__ double operator()(int s) const {
     if (resid) return rp[s];
     const Partial p = prow[s];
-    return p.s > 0.0 ? p.s * (double)scaled_exp(p.m - Mp, c) * invSp : 0.0;
+    // the factor is formed whether or not the unit has mass, so that both
+    // fields of the partial are requested together (a unit without mass,
+    // s = 0, weighs 0; its m of -FLT_MAX gives a factor of 0, never NaN)
+    const double f = (double)scaled_exp(p.m - Mp, c);
+    return p.s > 0.0 ? p.s * f * invSp : 0.0;
   }
 };
 
@@ -635,7 +639,22 @@ __device__ void find_unit(const UnitMass& um, int nunits, double w, int lane, do
   }
 }
 
-// Weights of the ids [id0, id0 + E) of a unit ending at s1 (0 past s1 and at y).
+// Weights of the ids [id0, id0 + E) from their logits vt (target) and vd
+// (draft; residual weights only), 0 past s1 and at y.
+template <class L, class WF>
+__device__ __forceinline__ void chunk_weights(const float* vt, const float* vd, int id0, int s1,
+                                              int y, const WF& wf, float* w) {
+#pragma unroll
+  for (int e = 0; e < L::E; ++e) {
+    float x;
+    if constexpr (std::is_same<WF, ResidW>::value) x = wf(vt[e], vd[e]);
+    else x = wf(vt[e]);
+    w[e] = (id0 + e < s1 && id0 + e != y) ? x : 0.f;
+  }
+}
+
+// Weights of the ids [id0, id0 + E) of a unit ending at s1 (0 past s1 and at y),
+// loading them element by element where the chunk crosses s1.
 template <class L, class WF>
 __device__ __forceinline__ void unit_weights(const typename L::Elem* tp, const typename L::Elem* dp,
                                              int id0, int s1, int y, const WF& wf, float* w) {
@@ -651,14 +670,32 @@ __device__ __forceinline__ void unit_weights(const typename L::Elem* tp, const t
       vd[e] = (dp && id0 + e < s1) ? L::one(dp + id0 + e) : 0.f;
     }
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float x;
-    if constexpr (std::is_same<WF, ResidW>::value) x = wf(vt[e], vd[e]);
-    else x = wf(vt[e]);
-    w[e] = (id0 + e < s1 && id0 + e != y) ? x : 0.f;
-  }
+  chunk_weights<L>(vt, vd, id0, s1, y, wf, w);
 }
+
+// The chunks of one thread's span [v0, v0 + PER) that lies wholly before s1,
+// requested together (one load latency for the span instead of one per chunk).
+template <class L, int PER, bool RESID>
+struct SpanRaw {
+  typename L::Raw t[PER / L::E];
+  typename L::Raw d[RESID ? PER / L::E : 1];
+  __device__ __forceinline__ void load(const typename L::Elem* tp, const typename L::Elem* dp,
+                                       int v0) {
+#pragma unroll
+    for (int c = 0; c < PER / L::E; ++c) {
+      t[c] = L::load(tp + v0 + c * L::E);
+      if constexpr (RESID) d[c] = L::load(dp + v0 + c * L::E);
+    }
+  }
+  template <class WF>
+  __device__ __forceinline__ void weights(int c, int id0, int s1, int y, const WF& wf,
+                                          float* w) const {
+    float vt[L::E], vd[L::E];
+    L::unpack(t[c], vt);
+    if constexpr (RESID) L::unpack(d[c], vd);
+    chunk_weights<L>(vt, vd, id0, s1, y, wf, w);
+  }
+};
 
 // Rescan one unit of PER * kBlock ids: thread t (< kBlock) sums the weights of
 // its PER ids in ascending order, a block-wide exclusive scan of those sums
@@ -679,15 +716,25 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid >> 6;
+  constexpr bool kResid = std::is_same<WF, ResidW>::value;
   const bool active = tid < kBlock;
   const int v0 = s0 + tid * PER;
+  // every thread's span lies wholly before s1 except where the unit ends:
+  // there chunks load one by one (and always on unaligned rows, whose
+  // one-element chunks would take a register per id)
+  const bool whole = L::E > 1 && v0 + PER <= s1;
   float keep[KEEP ? PER : 1];
+  SpanRaw<L, PER, kResid> raw;
   double ts = 0.0;
   if (active) {
+    if (whole) raw.load(tp, dp, v0);
 #pragma unroll
     for (int c = 0; c < PER / E; ++c) {
       float w[E];
-      unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
+      if (whole)
+        raw.weights(c, v0 + c * E, s1, y, wf, w);
+      else
+        unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         ts += (double)w[e];
@@ -695,13 +742,22 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
       }
     }
   }
-  // weights of chunk c for the walks below
+  // weights of chunk c for the walks below (without KEEP, the walking thread
+  // requests its span again first: reload())
+  auto reload = [&]() {
+    if constexpr (!KEEP) {
+      if (whole) raw.load(tp, dp, v0);
+    }
+  };
   auto chunk = [&](int c, float* w) {
     if constexpr (KEEP) {
 #pragma unroll
       for (int e = 0; e < E; ++e) w[e] = keep[c * E + e];
     } else {
-      unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
+      if (whole)
+        raw.weights(c, v0 + c * E, s1, y, wf, w);
+      else
+        unit_weights<L>(tp, dp, v0 + c * E, s1, y, wf, w);
     }
   };
   const double incl_w = wave_incl_scan(ts, lane);
@@ -726,6 +782,7 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
     __syncthreads();
     owner = *s_owner;
     if (tid == owner) {
+      reload();
       int tok = -1;
 #pragma unroll
       for (int c = 0; c < PER / E; ++c) {
@@ -741,6 +798,7 @@ __device__ int rescan_unit(const typename L::Elem* tp, const typename L::Elem* d
     return -2;
   }
   if (tid != owner) return -2;
+  reload();
   double cum = excl;
   double lo = 0.0, hi = 0.0;
   int tok = -1, last = -1;
