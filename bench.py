@@ -12,9 +12,9 @@ k_b per step / step time).  `roofline` describes the row-statistics kernel:
 algorithmic bytes (every logit row it must read, once) over its average
 duration measured with HIP events recorded around it on the call's stream.
 `other_path` times the other entry point (early exit vs all rows) on the same
-batch.  `--workload tree` measures greedy token-tree verification instead (32
+batch.  `--workload ddtree_budget32_v151936` measures greedy token-tree verification instead (32
 trees of 33 nodes over V = 151936 bf16; positions = draft nodes), and
-`--workload adaptive` the confidence-driven length choice plus the gather of
+`--workload adaptive_block7_v262144` the confidence-driven length choice plus the gather of
 the kept draft rows (512 blocks of 7 over V = 262144 bf16).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload.
 """
@@ -36,7 +36,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec and achieved HBM GB/s vs peak (1× MI355X)"
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "tree": "tree", "adaptive": "adaptive"}
+WORKLOADS = {"tiny_stochastic": 1, "greedy_v32000": 2, "stochastic_f32_v128256": 3,
+             "dflash_block16_v151936": 4, "ragged_mixed_v262144": 5,
+             "ddtree_budget32_v151936": "tree", "adaptive_block7_v262144": "adaptive"}
 CSRC = os.path.join(ROOT, "draft_token_verification_row_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -501,7 +503,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="ragged_mixed_v262144", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle (CPU baseline and parity against it)")
     ap.add_argument("--no-configs", action="store_true",
@@ -546,9 +548,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     sv.spec_verify_set_launch_plan({"auto": 0, "multi": 1, "single": 2}[args.launch_plan])
-    if args.workload == "tree":
+    if WORKLOADS[args.workload] == "tree":
         return bench_tree(args, sv, torch)
-    if args.workload == "adaptive":
+    if WORKLOADS[args.workload] == "adaptive":
         return bench_adaptive(args, sv, torch)
     cfg_id = WORKLOADS[args.workload]
     shard_kw = {}

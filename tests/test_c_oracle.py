@@ -54,16 +54,16 @@ def _agree(batch_np: dict, label: str, threads: int = 2):
 
 
 WORKLOADS = [
-    ("c1_full", 1, {}),
-    ("c2_greedy", 2, dict(B=16, V=32000)),
-    ("c3_f32_V40003", 3, dict(B=6, V=40003)),
-    ("c4_bf16_block16", 4, dict(B=2, V=20011)),
-    ("c5_mixed_V70001", 5, dict(B=16, V=70001)),
-    ("c5_strided", 5, dict(B=8, V=9999, target_ld=10001)),
+    ("tiny_full", 1, {}),
+    ("greedy_V32000", 2, dict(B=16, V=32000)),
+    ("f32_V40003", 3, dict(B=6, V=40003)),
+    ("block16_bf16", 4, dict(B=2, V=20011)),
+    ("mixed_V70001", 5, dict(B=16, V=70001)),
+    ("mixed_strided", 5, dict(B=8, V=9999, target_ld=10001)),
     ("k0_all", 5, dict(B=12, V=5000, k=0)),
-    ("c4_tiny_vocab", 4, dict(B=40, V=64)),
-    ("c3_vocab_1", 3, dict(B=4, V=1, k=2)),
-    ("c5_many_requests", 5, dict(B=600, V=300)),
+    ("block16_tiny_vocab", 4, dict(B=40, V=64)),
+    ("f32_vocab_1", 3, dict(B=4, V=1, k=2)),
+    ("mixed_many_requests", 5, dict(B=600, V=300)),
 ]
 
 

@@ -60,17 +60,17 @@ def _assert_same_as_all_rows(batch, got, full, label):
 
 
 CASES = [
-    ("c1_full", 1, {}, 0),
-    ("c2_full", 2, {}, 0),
-    ("c3_f32_V40003", 3, dict(B=8, V=40003), 0),
-    ("c4_bf16_V151936", 4, dict(B=3), 3),
-    ("c5_mixed_V70001", 5, dict(B=24, V=70001), 0),
-    ("c5_strided_scalar", 5, dict(B=12, V=9999, target_ld=10001), 1),
+    ("tiny_full", 1, {}, 0),
+    ("greedy_full", 2, {}, 0),
+    ("f32_V40003", 3, dict(B=8, V=40003), 0),
+    ("block16_bf16_V151936", 4, dict(B=3), 3),
+    ("mixed_V70001", 5, dict(B=24, V=70001), 0),
+    ("mixed_strided_scalar", 5, dict(B=12, V=9999, target_ld=10001), 1),
     ("k0_all_mixed", 5, dict(B=16, V=20000, k=0), 0),
-    ("c4_tiny_vocab", 4, dict(B=64, V=64), 0),
-    ("c3_vocab_1", 3, dict(B=4, V=1, k=2), 0),
-    ("c5_many_requests", 5, dict(B=2100, V=300), 2),
-    ("c2_greedy_odd_V", 2, dict(B=40, V=33333), 5),
+    ("block16_tiny_vocab", 4, dict(B=64, V=64), 0),
+    ("f32_vocab_1", 3, dict(B=4, V=1, k=2), 0),
+    ("mixed_many_requests", 5, dict(B=2100, V=300), 2),
+    ("greedy_odd_V", 2, dict(B=40, V=33333), 5),
 ]
 
 

@@ -28,23 +28,23 @@ def _log(msg):
 
 
 SMALL = [
-    ("c1_full", 1, {}),
-    ("c2_full", 2, {}),
-    ("c3_f32_V40003", 3, dict(B=8, V=40003)),
-    ("c4_bf16_V151936", 4, dict(B=3)),
-    ("c5_mixed_V70001", 5, dict(B=24, V=70001)),
-    ("c5_strided_vec", 5, dict(B=12, V=50000, target_ld=50048)),
-    ("c5_strided_scalar", 5, dict(B=12, V=9999, target_ld=10001)),
-    ("c3_f32_strided_scalar", 3, dict(B=6, V=4099, target_ld=4101)),
+    ("tiny_full", 1, {}),
+    ("greedy_full", 2, {}),
+    ("f32_V40003", 3, dict(B=8, V=40003)),
+    ("block16_bf16_V151936", 4, dict(B=3)),
+    ("mixed_V70001", 5, dict(B=24, V=70001)),
+    ("mixed_strided_vec", 5, dict(B=12, V=50000, target_ld=50048)),
+    ("mixed_strided_scalar", 5, dict(B=12, V=9999, target_ld=10001)),
+    ("f32_strided_scalar", 3, dict(B=6, V=4099, target_ld=4101)),
     ("k0_all_mixed", 5, dict(B=16, V=20000, k=0)),
-    ("c4_tiny_vocab", 4, dict(B=64, V=64)),
-    ("c3_vocab_1", 3, dict(B=4, V=1, k=2)),
-    ("c5_many_requests", 5, dict(B=2100, V=300)),
-    ("c2_greedy_odd_V", 2, dict(B=40, V=33333)),
+    ("block16_tiny_vocab", 4, dict(B=64, V=64)),
+    ("f32_vocab_1", 3, dict(B=4, V=1, k=2)),
+    ("mixed_many_requests", 5, dict(B=2100, V=300)),
+    ("greedy_odd_V", 2, dict(B=40, V=33333)),
     # more rows than k_stats plans in LDS (2K + B > 6144 with B <= 2048): the
     # separate plan kernel writes the row lists
-    ("c5_rows_beyond_lds_plan", 5, dict(B=600, V=3001, k=7)),
-    ("c3_greedy_free_rows_beyond_lds_plan", 3, dict(B=400, V=2000, k=8)),
+    ("mixed_rows_beyond_lds_plan", 5, dict(B=600, V=3001, k=7)),
+    ("f32_rows_beyond_lds_plan", 3, dict(B=400, V=2000, k=8)),
 ]
 
 
