@@ -3,6 +3,7 @@ dtype, vocabulary, ragged k, greedy share, temperature, logit scale, strided
 rows, masked columns) against the fp64 oracle, through both launch plans of the
 all-rows entry points (bit for bit equal to each other) and through early exit
 (bit for bit equal to the all-rows path at the tested positions).  Needs the GPU."""
+import os
 import sys
 
 import numpy as np
@@ -14,7 +15,9 @@ from tests.parity import compare, run_hip, run_oracle
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-SEEDS = list(range(150))
+# SPEC_VERIFY_RANDOM_SEEDS="lo:hi" sweeps other seeds (default the first 150)
+_lo, _hi = (int(x) for x in os.environ.get("SPEC_VERIFY_RANDOM_SEEDS", "0:150").split(":"))
+SEEDS = list(range(_lo, _hi))
 
 
 def _plan(sv, plan, batch):
