@@ -288,7 +288,8 @@ struct TreeSizes {
 bool compute_tree_sizes(long long B, long long N, long long V, TreeSizes* z) {
   if (B < 1 || N < B || V < 1 || V > (1ll << 30)) return false;
   if (N >= (1ll << 29)) return false;
-  const long long nseg = (V + kSegMinElems - 1) / kSegMinElems;
+  // 4 KiB units (the rounds) outnumber 32 KiB units (all node rows), so the
+  // partials are sized for the former
   const long long ntseg = (V + kTreeSegBytes / 4 - 1) / (kTreeSegBytes / 4);
   if (N * ntseg >= (1ll << 31)) return false;
   const long long npart = N * ntseg;   // every node row, in 32 KiB (all rows) or 4 KiB units
