@@ -57,3 +57,37 @@ def test_c_oracle_baseline_helpers():
     bad = dict(res, out_tokens=res["out_tokens"].copy())
     bad["out_tokens"][0] += 1
     assert not bench.oracles_agree(b, bad, ref)
+
+
+def test_parity_summary_classifies_requests():
+    """The bench's parity field: equal requests pass, a stochastic request that
+    differs with the oracle's deciding margin below 1e-6 is a near-tie, any
+    other difference (or any greedy difference) is a mismatch."""
+    import synth
+    b = synth.make_batch(5, "cpu", B=6, V=500)
+    ref = bench.oracle_inputs(b, chunk=6)
+    import oracle
+    want = oracle.verify_batch(**ref[0])
+    got = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in want.items()}
+    got["p_draft"] = want["p_draft"].astype(np.float32)
+    got["q_draft"] = want["q_draft"].astype(np.float32)
+    assert bench.parity_summary(b, got, want)["mismatches"] == 0
+    off = b.offsets
+    stoch = [i for i in range(b.B) if not b.greedy[i]]
+    greedy = [i for i in range(b.B) if b.greedy[i]]
+    assert stoch and greedy
+    s, g = stoch[0], greedy[0]
+    bad = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in got.items()}
+    slot = int(off[s]) + s + int(want["accepted_len"][s])
+    bad["out_tokens"][slot] = (int(bad["out_tokens"][slot]) + 1) % b.V
+    tight = dict(want, margin=want["margin"].copy())
+    tight["margin"][s] = 5e-7
+    r = bench.parity_summary(b, bad, tight)
+    assert (r["mismatches"], r["near_ties"]) == (0, 1), r
+    tight["margin"][s] = 2e-6
+    r = bench.parity_summary(b, bad, tight)
+    assert (r["mismatches"], r["near_ties"]) == (1, 0), r
+    badg = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in got.items()}
+    badg["accepted_len"][g] = int(badg["accepted_len"][g]) + 1
+    r = bench.parity_summary(b, badg, want)
+    assert (r["mismatches"], r["near_ties"]) == (1, 0), r
